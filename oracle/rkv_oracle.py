@@ -1,0 +1,192 @@
+"""CPU oracle for the R-KV decode-time KV-cache compression step.
+
+TEST INFRASTRUCTURE ONLY.  Only tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The product path (the HIP
+library and its Python binding) never calls it, and this module imports
+nothing from the product path.
+
+Plain, slow, float64.  Every function follows one step of the method as the
+pages describe it; where they are silent the plainest reading is taken and
+named in the docstring.  Sources:
+
+* [PROJ] R-KV project page (hysenlabs.com, "R-KV: Redundancy-Aware KV Cache
+  Compression for Reasoning Models"): section "How R-KV decides what to drop:
+  budget, buffer and cross-layer scoring" (decode-time trigger on budget and
+  buffer, a local window, mix_lambda blending two scores, FREE_BLOCKS
+  returning evicted blocks), and the command block of "Installing R-KV and
+  running a first math evaluation" (kv_budget 1024, window_size 8,
+  mix_lambda 0.1, divide_length 128).
+* [BLOG] hotdry blog post on R-KV, EvolKV and Ada-KV, section on R-KV:
+  redundancy from cosine similarity of key vectors, importance from
+  multi-head attention, eviction that favours high importance and low
+  redundancy, lambda near 0.1.  Section on risks: pure attention scoring
+  (SnapKV-like) is the lambda = 1 case.
+
+Numbers: bf16 inputs are widened exactly to float64; all arithmetic is float64.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+__all__ = [
+    "decode", "is_triggered", "window_logits", "importance", "cosine_gram",
+    "redundancy", "mixed_score", "score_unit", "select_keep", "compact_rows",
+    "free_blocks", "unit_step", "q_group", "step_contiguous", "step_unit",
+]
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage values -> float64.  bf16 is stored as its 16 bit pattern, which
+    is the top half of the float32 with the same value."""
+    if dtype == "bf16":
+        w = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return w.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def is_triggered(n: int, budget: int, buffer: int) -> bool:
+    """[PROJ] "How R-KV decides what to drop": compression runs at decode time
+    once the cache has grown by a buffer beyond the budget.  Reading: a
+    sequence of n cached tokens triggers iff n >= budget + buffer (with the
+    HF path's step_length division, buffer = divide_length)."""
+    return int(n) >= int(budget) + int(buffer)
+
+
+def window_logits(q_rows: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Scaled dot products q.k / sqrt(d) of the window queries against every
+    cached key: (G*w, d) x (N, d) -> (G*w, N)."""
+    d = k.shape[1]
+    return (q_rows @ k.T) / math.sqrt(d)
+
+
+def importance(q_rows: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """[BLOG] R-KV section: importance of a cached token comes from the
+    attention the model pays it; [PROJ]: the last window_size queries do the
+    scoring.  Reading: each of the G*w rows (the window's queries of every
+    query head sharing this kv head) is a softmax over all N cached keys, no
+    causal mask inside the window, scale 1/sqrt(d); the importance of token j
+    is the mean of its attention weight over those rows."""
+    logits = window_logits(q_rows, k)
+    logits = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p.mean(axis=0)
+
+
+def cosine_gram(k: np.ndarray) -> np.ndarray:
+    """[BLOG] R-KV section: redundancy is measured by cosine similarity between
+    key vectors.  Returns the N x N matrix of cosines of the L2-normalised keys
+    (a zero key normalises to the zero vector)."""
+    norms = np.sqrt((k * k).sum(axis=1))
+    safe = np.where(norms > 0, norms, 1.0)
+    khat = np.where(norms[:, None] > 0, k / safe[:, None], 0.0)
+    return khat @ khat.T
+
+
+def redundancy(k: np.ndarray) -> np.ndarray:
+    """Mean off-diagonal cosine similarity of each key to the other N - 1 keys
+    of the same (sequence, layer, kv head), over all N keys (window included)."""
+    n = k.shape[0]
+    assert n >= 2
+    c = cosine_gram(k)
+    off = c.sum(axis=1) - np.diag(c)
+    return off / (n - 1)
+
+
+def mixed_score(imp: np.ndarray, red: np.ndarray, lam: float) -> np.ndarray:
+    """[PROJ] mix_lambda blends the two signals; [BLOG] keep high importance
+    and low redundancy.  S = lam * I - (1 - lam) * R, larger is kept.  No
+    normalisation of either score before mixing (none is described)."""
+    return lam * imp - (1.0 - lam) * red
+
+
+def score_unit(q_rows: np.ndarray, k: np.ndarray, lam: float):
+    """(I, R, S) for one (sequence, layer, kv head)."""
+    imp = importance(q_rows, k)
+    red = redundancy(k)
+    return imp, red, mixed_score(imp, red, lam)
+
+
+def select_keep(scores: np.ndarray, n: int, budget: int, window: int) -> np.ndarray:
+    """Keep set of one unit: the last `window` tokens always, plus the
+    budget - window best candidates of [0, n - window) ranked by score
+    descending, equal scores broken by lower position first.  Returned in
+    ascending position order (slot i of the compacted cache holds keep[i]).
+    Reading: the budget counts the window ([PROJ] names budget and window
+    separately; the compacted cache then holds exactly `budget` tokens)."""
+    assert 0 < window < budget <= n
+    cand = n - window
+    s = np.asarray(scores[:cand], dtype=np.float64)
+    pos = np.arange(cand)
+    order = np.lexsort((pos, -s))          # primary: -s ascending; then position
+    chosen = np.sort(order[: budget - window])
+    return np.concatenate([chosen, np.arange(cand, n)]).astype(np.int64)
+
+
+def compact_rows(rows: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """Slot i of the compacted cache receives row keep[i] ([PROJ]: two-phase
+    compaction of the kept entries).  Plain fancy indexing."""
+    return rows[np.asarray(keep)]
+
+
+def free_blocks(bt_row: Sequence[int], n: int, budget: int, block_size: int) -> List[int]:
+    """[PROJ] FREE_BLOCKS: blocks emptied by compaction go back to the
+    allocator.  After compaction the sequence holds `budget` tokens in its
+    first ceil(budget/bs) logical blocks; logical blocks ceil(budget/bs) ..
+    ceil(n/bs)-1 are freed, reported as physical ids in logical order."""
+    first = -(-budget // block_size)
+    last = -(-n // block_size)
+    return [int(bt_row[b]) for b in range(first, last)]
+
+
+def unit_step(q_rows, k, k_store, v_store, budget, window, lam):
+    """Everything one unit produces: I, R, S, keep, K', V'.  q_rows and k are
+    float64; k_store and v_store are the same rows in storage dtype, so that
+    the compacted rows are the input bits."""
+    n = k.shape[0]
+    imp, red, s = score_unit(q_rows, k, lam)
+    keep = select_keep(s, n, budget, window)
+    return dict(imp=imp, red=red, score=s, keep=keep,
+                k_new=compact_rows(k_store, keep), v_new=compact_rows(v_store, keep))
+
+
+def q_group(q_seq_layer: np.ndarray, h: int, group: int) -> np.ndarray:
+    """Window-query rows of the query heads that share kv head h (GQA: query
+    head j uses kv head j // group): (group, w, d) -> (group*w, d)."""
+    qg = q_seq_layer[h * group:(h + 1) * group]
+    return qg.reshape(-1, qg.shape[-1])
+
+
+def step_contiguous(spec, k, v, q, lens) -> Dict[str, object]:
+    """Whole step over contiguous caches k, v (L, S, Hkv, cap, d) and window
+    queries q (L, S, Hq, w, d), all in storage dtype.  Returns per-unit results
+    of triggered sequences and the new lengths.  Meant for small cases."""
+    group = spec.num_q_heads // spec.num_kv_heads
+    out = {"units": {}, "lens": np.array(lens, dtype=np.int64).copy()}
+    for s in range(spec.num_seqs):
+        n = int(lens[s])
+        if not is_triggered(n, spec.budget, spec.buffer):
+            continue
+        for l in range(spec.num_layers):
+            qd = decode(q[l, s], spec.dtype)
+            for h in range(spec.num_kv_heads):
+                out["units"][(s, l, h)] = unit_step(
+                    q_group(qd, h, group), decode(k[l, s, h, :n], spec.dtype),
+                    k[l, s, h, :n], v[l, s, h, :n], spec.budget, spec.window,
+                    spec.mix_lambda)
+        out["lens"][s] = spec.budget
+    return out
+
+
+def step_unit(spec, q_sl, k_rows, v_rows, h):
+    """One unit given its window queries (Hq, w, d) and its N key and value
+    rows in logical order (storage dtype), e.g. gathered from a paged pool."""
+    group = spec.num_q_heads // spec.num_kv_heads
+    qd = decode(q_sl, spec.dtype)
+    return unit_step(q_group(qd, h, group), decode(k_rows, spec.dtype), k_rows, v_rows,
+                     spec.budget, spec.window, spec.mix_lambda)

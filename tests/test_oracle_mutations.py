@@ -1,0 +1,81 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them.  A mutant that survives would mean the pins
+do not constrain that part of the oracle."""
+import importlib.util
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+pytestmark = pytest.mark.cpu
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "rkv_oracle.py")
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("no 1/sqrt(d) scale", "return (q_rows @ k.T) / math.sqrt(d)", "return (q_rows @ k.T)"),
+    ("scale 1/d", "return (q_rows @ k.T) / math.sqrt(d)", "return (q_rows @ k.T) / d"),
+    ("softmax over the wrong axis", "p = p / p.sum(axis=1, keepdims=True)",
+     "p = p / p.sum(axis=0, keepdims=True)"),
+    ("sum instead of mean over rows", "return p.mean(axis=0)", "return p.sum(axis=0)"),
+    ("max over the wrong axis", "logits - logits.max(axis=1, keepdims=True)",
+     "logits - logits.max()"),
+    ("diagonal kept", "off = c.sum(axis=1) - np.diag(c)", "off = c.sum(axis=1)"),
+    ("divide by N", "return off / (n - 1)", "return off / n"),
+    ("no key normalisation", "return khat @ khat.T", "return k @ k.T"),
+    ("norm without sqrt", "norms = np.sqrt((k * k).sum(axis=1))", "norms = (k * k).sum(axis=1)"),
+    ("mix sign flipped", "return lam * imp - (1.0 - lam) * red", "return lam * imp + (1.0 - lam) * red"),
+    ("lambda roles swapped", "return lam * imp - (1.0 - lam) * red", "return (1.0 - lam) * imp - lam * red"),
+    ("ties keep the later position", "order = np.lexsort((pos, -s))", "order = np.lexsort((-pos, -s))"),
+    ("ascending score kept", "order = np.lexsort((pos, -s))", "order = np.lexsort((pos, s))"),
+    ("window not forced", "chosen = np.sort(order[: budget - window])",
+     "chosen = np.sort(order[: budget - window]); cand = n"),
+    ("budget excludes window", "chosen = np.sort(order[: budget - window])",
+     "chosen = np.sort(order[: budget])"),
+    ("free blocks floor", "first = -(-budget // block_size)", "first = budget // block_size"),
+    ("trigger strict", "return int(n) >= int(budget) + int(buffer)",
+     "return int(n) > int(budget) + int(buffer)"),
+    ("rows reversed before the row mean", "return (q_rows @ k.T) / math.sqrt(d)",
+     "return (k @ q_rows.T).T[::-1] / math.sqrt(d)"),
+    ("GQA heads strided", "qg = q_seq_layer[h * group:(h + 1) * group]",
+     "qg = q_seq_layer[h::q_seq_layer.shape[0] // group]"),
+    ("transposed Gram operand", "return khat @ khat.T", "return khat.T @ khat"),
+    ("gather off by one", "return rows[np.asarray(keep)]", "return rows[np.minimum(np.asarray(keep) + 1, len(rows) - 1)]"),
+]
+
+# Mathematically neutral edits: the pins must NOT reject these (softmax is
+# invariant to a per-row or global shift).
+NEUTRAL = {"max over the wrong axis", "rows reversed before the row mean"}
+
+
+def _mutant(old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) >= 1, f"mutation target vanished: {old!r}"
+    text = text.replace(old, new, 1)
+    mod = types.ModuleType("rkv_oracle_mutant")
+    mod.__file__ = SRC
+    exec(compile(text, SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def _run_pins(mod):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant(name, old, new):
+    failed = _run_pins(_mutant(old, new))
+    if name in NEUTRAL:
+        assert not failed, f"neutral edit rejected by {failed}"
+    else:
+        assert failed, f"mutant '{name}' survived every pin"
