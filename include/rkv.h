@@ -1,0 +1,172 @@
+/*
+ * rkv.h -- C ABI of the R-KV decode-time KV-cache compression step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step (R-KV project page on hysenlabs.com, "R-KV: Redundancy-Aware KV
+ * Cache Compression for Reasoning Models", section "How R-KV decides what to
+ * drop: budget, buffer and cross-layer scoring"; hotdry blog post on R-KV /
+ * EvolKV / Ada-KV, R-KV section) runs for every sequence whose cache has
+ * reached budget + buffer tokens.  For each triggered (sequence, layer, kv
+ * head) -- a "unit" -- it
+ *   1. scores each cached token j:
+ *        importance  I_j = mean over the window queries of the query heads
+ *                          that share the kv head of softmax_j(q . k_j / sqrt(d))
+ *                          (softmax over all N cached keys),
+ *        redundancy  R_j = mean cosine similarity of k_j to the other N-1 keys,
+ *        score       S_j = lambda * I_j - (1 - lambda) * R_j;
+ *   2. keeps the last `window` tokens and the best budget - window of the
+ *      others (larger S first, equal S: lower position first);
+ *   3. compacts K and V in place so that slot i holds the i-th kept token in
+ *      position order; the sequence then holds `budget` tokens, and in the
+ *      paged layout the emptied blocks are reported (FREE_BLOCKS).
+ *
+ * Conventions for every call
+ *   - Device pointers are caller-owned; the library never allocates, frees or
+ *     keeps them.  Host pointers are read (and, where stated, written) during
+ *     the call only.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     is asynchronous: results are valid once the stream reaches that point.
+ *   - Every argument is checked before anything is enqueued.  On an error the
+ *     call returns a status other than RKV_OK, enqueues nothing and changes no
+ *     output; rkv_last_error() then describes it.  No C++ exception crosses
+ *     this interface.  A device fault of earlier work shows up as RKV_ERR_HIP.
+ *   - Sequence lengths live on the host.  Sequences below the trigger are
+ *     untouched: their cache rows, score rows and keep rows are not written.
+ *   - A call covers all layers and all triggered sequences of the batch.
+ *
+ * Layouts (row-major, element = the cache dtype unless stated)
+ *   contiguous K, V : [num_layers][num_seqs][num_kv_heads][capacity][head_dim]
+ *   paged K, V pool : [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ *                     token t of sequence s lives in physical block
+ *                     block_table[s * max_blocks_per_seq + t / block_size],
+ *                     row t % block_size; every layer uses the same table.
+ *   window queries  : [num_layers][num_seqs][num_q_heads][window][head_dim]
+ *                     query head j belongs to kv head j / (num_q_heads / num_kv_heads)
+ *   scores, I, R    : float32 [num_layers][num_seqs][num_kv_heads][score_stride]
+ *   keep            : int32   [num_layers][num_seqs][num_kv_heads][budget]
+ */
+#ifndef RKV_H_
+#define RKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rkv_status {
+  RKV_OK = 0,
+  RKV_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent arguments   */
+  RKV_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels handle  */
+  RKV_ERR_WORKSPACE = 3,    /* workspace missing or too small                   */
+  RKV_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed       */
+} rkv_status;
+
+typedef enum rkv_dtype { RKV_DTYPE_F32 = 0, RKV_DTYPE_BF16 = 1 } rkv_dtype;
+typedef enum rkv_layout { RKV_LAYOUT_CONTIGUOUS = 0, RKV_LAYOUT_PAGED = 1 } rkv_layout;
+
+/* Longest cache (tokens per sequence) the kernels accept. */
+#define RKV_MAX_LEN 32768
+/* Largest num_q_heads / num_kv_heads * window the scoring kernels accept. */
+#define RKV_MAX_WINDOW_ROWS 142
+
+/* The method's knobs (the HF flags kv_budget, window_size, mix_lambda and
+ * divide_length on the R-KV project page, section "Installing R-KV and running
+ * a first math evaluation"; budget and buffer as in "How R-KV decides what to
+ * drop") plus the model and cache shape. */
+typedef struct rkv_config {
+  int32_t num_layers;     /* >= 1                                               */
+  int32_t num_q_heads;    /* >= 1, a multiple of num_kv_heads                   */
+  int32_t num_kv_heads;   /* >= 1                                               */
+  int32_t head_dim;       /* 64 or 128                                          */
+  int32_t budget;         /* B > window: tokens kept per unit, window included  */
+  int32_t buffer;         /* > 0: a sequence triggers iff len >= budget+buffer  */
+  int32_t window;         /* w >= 1: window queries, and tokens always kept     */
+  float mix_lambda;       /* lambda in [0, 1]                                   */
+  int32_t dtype;          /* rkv_dtype of K, V and the window queries           */
+  int32_t layout;         /* rkv_layout of K and V                              */
+  int32_t block_size;     /* paged: tokens per block (>= 1); ignored otherwise  */
+} rkv_config;
+
+/* The KV cache the step reads and compacts (device memory, caller-owned). */
+typedef struct rkv_cache {
+  void *k;                          /* keys   (layout above)                    */
+  void *v;                          /* values (same layout as k)                */
+  int32_t capacity;                 /* contiguous: token slots per (l, s, h)    */
+  int32_t num_blocks;               /* paged: blocks per layer in the pool      */
+  const int32_t *block_table;       /* paged: device int32 [num_seqs][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;       /* paged                                    */
+} rkv_cache;
+
+/* Text of a status code (static storage). */
+const char *rkv_status_string(rkv_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char *rkv_last_error(void);
+
+/* 1 if a sequence of `len` cached tokens triggers (len >= budget + buffer),
+ * else 0; the rule of "How R-KV decides what to drop".  Returns -1 if cfg is
+ * NULL. */
+int32_t rkv_is_triggered(const rkv_config *cfg, int32_t len);
+
+/* Bytes of device workspace rkv_score needs for any batch of at most
+ * num_seqs sequences of at most max_len tokens.  0 on invalid arguments. */
+size_t rkv_workspace_size(const rkv_config *cfg, int32_t num_seqs, int32_t max_len);
+
+/* Step 1, scoring: I, R and S of every cached token of every triggered unit,
+ * all layers in one pass ("batched cross-layer scoring" on the R-KV project
+ * page; the two signals and their blend in the blog's R-KV section).
+ *   q_window   device, window queries (layout above)
+ *   h_seq_lens host int32 [num_seqs], current cache lengths
+ *   scores     device float32 (layout above), columns [0, len) of triggered
+ *              rows written; score_stride >= the longest triggered length
+ *   importance, redundancy  device float32 like scores, or NULL to skip
+ *   workspace  device, >= rkv_workspace_size(cfg, num_seqs, max len), 256-byte
+ *              aligned; contents on entry are ignored
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED (head_dim, window rows,
+ * length above RKV_MAX_LEN), RKV_ERR_WORKSPACE, RKV_ERR_HIP. */
+rkv_status rkv_score(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
+                     int32_t num_seqs, const int32_t *h_seq_lens,
+                     float *scores, int32_t score_stride,
+                     float *importance, float *redundancy,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step 2, selection: for each triggered unit, keep[0 .. budget-window) = the
+ * chosen candidates of [0, len-window) in ascending position order, and
+ * keep[budget-window .. budget) = len-window .. len-1 (the window).  Candidates
+ * are ranked by score descending, ties by lower position; -0.0 ranks equal to
+ * +0.0.  NaN scores give an unspecified (but in-range, duplicate-free) set.
+ *   scores  device float32 (layout above), as written by rkv_score
+ *   keep    device int32 (layout above)
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP. */
+rkv_status rkv_select(const rkv_config *cfg, int32_t num_seqs, const int32_t *h_seq_lens,
+                      const float *scores, int32_t score_stride, int32_t *keep,
+                      void *stream);
+
+/* Step 3, compaction and FREE_BLOCKS ("two-phase compaction" and
+ * "bounded-footprint block freeing" on the R-KV project page): for each
+ * triggered unit, K and V slot i receive the row of token keep[i], in place;
+ * rows at slots >= budget are left as they were.  Then h_seq_lens[s] = budget
+ * for each triggered s.
+ * Paged layout: the physical ids of logical blocks ceil(budget/block_size) ..
+ * ceil(len/block_size)-1 of each triggered sequence are written to
+ * free_blocks (device int32), sequences in order, blocks in logical order;
+ * h_free_counts[s] (host, may be NULL) receives the count per sequence (0 for
+ * sequences not triggered).  The block table is not modified: returning the
+ * ids to an allocator is the caller's.  free_capacity = entries available in
+ * free_blocks.  Contiguous layout: free_blocks may be NULL; counts are 0.
+ *   keep  device int32 (layout above), ascending per unit, as from rkv_select
+ * Errors: RKV_ERR_INVALID_ARG (including free_capacity too small),
+ * RKV_ERR_UNSUPPORTED, RKV_ERR_HIP.  A keep row that is not strictly
+ * ascending within [0, len) is undefined behaviour. */
+rkv_status rkv_compact(const rkv_config *cfg, const rkv_cache *cache, int32_t num_seqs,
+                       int32_t *h_seq_lens, const int32_t *keep,
+                       int32_t *free_blocks, int32_t free_capacity,
+                       int32_t *h_free_counts, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H_ */

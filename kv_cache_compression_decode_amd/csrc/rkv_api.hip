@@ -1,0 +1,338 @@
+// Host side of the C ABI declared in include/rkv.h: argument checks, the
+// table of triggered sequences, workspace sizing and kernel launches.
+// Every check runs before anything is enqueued; errors are returned with a
+// thread-local detail message and never thrown across the interface.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "rkv.h"
+#include "rkv_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+rkv_status fail(rkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+rkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(RKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2_exact(int v) {
+  if (v < 1 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+rkv_status check_config(const rkv_config* c) {
+  if (c == nullptr) return fail(RKV_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->num_layers < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1)
+    return fail(RKV_ERR_INVALID_ARG, "num_layers, num_q_heads and num_kv_heads must be >= 1");
+  if (c->num_q_heads % c->num_kv_heads != 0)
+    return fail(RKV_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                c->num_q_heads, c->num_kv_heads);
+  if (c->window < 1) return fail(RKV_ERR_INVALID_ARG, "window must be >= 1");
+  if (c->budget <= c->window)
+    return fail(RKV_ERR_INVALID_ARG, "budget (%d) must exceed window (%d)", c->budget, c->window);
+  if (c->buffer < 1) return fail(RKV_ERR_INVALID_ARG, "buffer must be >= 1");
+  if (!(c->mix_lambda >= 0.f && c->mix_lambda <= 1.f))
+    return fail(RKV_ERR_INVALID_ARG, "mix_lambda must lie in [0, 1]");
+  if (c->dtype != RKV_DTYPE_F32 && c->dtype != RKV_DTYPE_BF16)
+    return fail(RKV_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (c->layout != RKV_LAYOUT_CONTIGUOUS && c->layout != RKV_LAYOUT_PAGED)
+    return fail(RKV_ERR_INVALID_ARG, "unknown layout %d", c->layout);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(RKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
+  if (c->layout == RKV_LAYOUT_PAGED) {
+    if (c->block_size < 1) return fail(RKV_ERR_INVALID_ARG, "block_size must be >= 1");
+    if (ilog2_exact(c->block_size) < 0 || c->block_size > 1024)
+      return fail(RKV_ERR_UNSUPPORTED, "block_size %d (supported: powers of two up to 1024)",
+                  c->block_size);
+  }
+  const long gw = (long)(c->num_q_heads / c->num_kv_heads) * c->window;
+  if (gw > RKV_MAX_WINDOW_ROWS)
+    return fail(RKV_ERR_UNSUPPORTED, "group * window = %ld exceeds %d", gw, RKV_MAX_WINDOW_ROWS);
+  if (c->budget > RKV_MAX_LEN)
+    return fail(RKV_ERR_UNSUPPORTED, "budget %d exceeds %d", c->budget, RKV_MAX_LEN);
+  return RKV_OK;
+}
+
+rkv_status check_cache(const rkv_config* c, const rkv_cache* k, bool need_v) {
+  if (k == nullptr) return fail(RKV_ERR_INVALID_ARG, "cache is NULL");
+  if (k->k == nullptr) return fail(RKV_ERR_INVALID_ARG, "cache->k is NULL");
+  if (need_v && k->v == nullptr) return fail(RKV_ERR_INVALID_ARG, "cache->v is NULL");
+  if (!aligned16(k->k) || (need_v && !aligned16(k->v)))
+    return fail(RKV_ERR_INVALID_ARG, "cache->k / cache->v must be 16-byte aligned");
+  if (c->layout == RKV_LAYOUT_CONTIGUOUS) {
+    if (k->capacity < 1) return fail(RKV_ERR_INVALID_ARG, "capacity must be >= 1");
+  } else {
+    if (k->num_blocks < 1) return fail(RKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+    if (k->block_table == nullptr) return fail(RKV_ERR_INVALID_ARG, "block_table is NULL");
+    if (k->max_blocks_per_seq < 1) return fail(RKV_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  }
+  return RKV_OK;
+}
+
+struct Trig {
+  int32_t seq, len;
+};
+
+// Triggered sequences, with length checks against the cache geometry.
+// `cache` may be NULL (selection needs no geometry).
+rkv_status collect(const rkv_config* c, const rkv_cache* cache, int32_t num_seqs,
+                   const int32_t* lens, std::vector<Trig>& out) {
+  out.clear();
+  if (num_seqs < 0) return fail(RKV_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs > 0 && lens == nullptr) return fail(RKV_ERR_INVALID_ARG, "h_seq_lens is NULL");
+  const long trigger = (long)c->budget + c->buffer;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t n = lens[s];
+    if (n < 0) return fail(RKV_ERR_INVALID_ARG, "h_seq_lens[%d] = %d is negative", s, n);
+    if (n < trigger) continue;
+    if (n > RKV_MAX_LEN)
+      return fail(RKV_ERR_UNSUPPORTED, "h_seq_lens[%d] = %d exceeds %d", s, n, RKV_MAX_LEN);
+    if (cache != nullptr) {
+      if (c->layout == RKV_LAYOUT_CONTIGUOUS && n > cache->capacity)
+        return fail(RKV_ERR_INVALID_ARG, "h_seq_lens[%d] = %d exceeds capacity %d", s, n,
+                    cache->capacity);
+      if (c->layout == RKV_LAYOUT_PAGED && (long)n > (long)cache->max_blocks_per_seq * c->block_size)
+        return fail(RKV_ERR_INVALID_ARG, "h_seq_lens[%d] = %d exceeds the block table (%d blocks)",
+                    s, n, cache->max_blocks_per_seq);
+    }
+    out.push_back({s, n});
+  }
+  return RKV_OK;
+}
+
+rkv::Geom make_geom(const rkv_config* c, const rkv_cache* cache, int32_t num_seqs) {
+  rkv::Geom g{};
+  g.num_seqs = num_seqs;
+  g.num_layers = c->num_layers;
+  g.hq = c->num_q_heads;
+  g.hkv = c->num_kv_heads;
+  g.group = c->num_q_heads / c->num_kv_heads;
+  g.d = c->head_dim;
+  g.window = c->window;
+  g.budget = c->budget;
+  g.paged = c->layout == RKV_LAYOUT_PAGED;
+  if (cache != nullptr) {
+    g.cap = cache->capacity;
+    g.nblk = cache->num_blocks;
+    g.maxblk = cache->max_blocks_per_seq;
+  }
+  g.bs_shift = g.paged ? ilog2_exact(c->block_size) : 0;
+  return g;
+}
+
+// Fill the triggered table for trig[first, first + count).
+void fill_table(rkv::TrigTable& tt, const std::vector<Trig>& trig, size_t first, int count,
+                const int32_t* free_off) {
+  for (int i = 0; i < count; ++i) {
+    tt.seq[i] = trig[first + i].seq;
+    tt.len[i] = trig[first + i].len;
+    tt.free_off[i] = free_off ? free_off[first + i] : 0;
+  }
+}
+
+int32_t max_len_of(const std::vector<Trig>& trig, size_t first, size_t count) {
+  int32_t m = 0;
+  for (size_t i = first; i < first + count; ++i) m = std::max(m, trig[i].len);
+  return m;
+}
+
+size_t record_floats(const rkv_config* c) {
+  return 2 * (size_t)(c->num_q_heads / c->num_kv_heads) * c->window + c->head_dim;
+}
+
+size_t ws_bytes_for(const rkv_config* c, long seqs, long max_len) {
+  const long t = std::min<long>(seqs, rkv::kMaxTrig);
+  const long chunks = (max_len + rkv::kChunk - 1) / rkv::kChunk;
+  const size_t bytes = (size_t)t * c->num_layers * c->num_kv_heads * chunks * record_floats(c) * 4;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rkv_status_string(rkv_status s) {
+  switch (s) {
+    case RKV_OK: return "RKV_OK";
+    case RKV_ERR_INVALID_ARG: return "RKV_ERR_INVALID_ARG";
+    case RKV_ERR_UNSUPPORTED: return "RKV_ERR_UNSUPPORTED";
+    case RKV_ERR_WORKSPACE: return "RKV_ERR_WORKSPACE";
+    case RKV_ERR_HIP: return "RKV_ERR_HIP";
+  }
+  return "RKV_ERR_UNKNOWN";
+}
+
+const char* rkv_last_error(void) { return g_err.c_str(); }
+
+int32_t rkv_is_triggered(const rkv_config* cfg, int32_t len) {
+  if (cfg == nullptr) return -1;
+  return (long)len >= (long)cfg->budget + cfg->buffer ? 1 : 0;
+}
+
+size_t rkv_workspace_size(const rkv_config* cfg, int32_t num_seqs, int32_t max_len) {
+  if (check_config(cfg) != RKV_OK || num_seqs < 0 || max_len < 0) return 0;
+  return ws_bytes_for(cfg, num_seqs, max_len);
+}
+
+rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* q_window,
+                     int32_t num_seqs, const int32_t* h_seq_lens, float* scores,
+                     int32_t score_stride, float* importance, float* redundancy, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  std::vector<Trig> trig;
+  if ((st = check_cache(cfg, cache, false)) != RKV_OK) return st;
+  if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
+  if (trig.empty()) return RKV_OK;
+  if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
+  if (!aligned16(q_window)) return fail(RKV_ERR_INVALID_ARG, "q_window must be 16-byte aligned");
+  if (scores == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores is NULL");
+  const int32_t maxn = max_len_of(trig, 0, trig.size());
+  if (score_stride < maxn)
+    return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
+                score_stride, maxn);
+  if (workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+    const size_t cnt = std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+    const size_t need = ws_bytes_for(cfg, (long)cnt, max_len_of(trig, first, cnt));
+    if (workspace_bytes < need)
+      return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  }
+
+  rkv::ScoreArgs a{};
+  a.g = make_geom(cfg, cache, num_seqs);
+  a.k = cache->k;
+  a.q = q_window;
+  a.bt = cache->block_table;
+  a.scores = scores;
+  a.imp = importance;
+  a.red = redundancy;
+  a.part = static_cast<float*>(workspace);
+  a.score_stride = score_stride;
+  a.gw = a.g.group * cfg->window;
+  a.rec = (int32_t)record_floats(cfg);
+  a.lambda = cfg->mix_lambda;
+  a.c = (float)(1.4426950408889634 / sqrt((double)cfg->head_dim));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+    const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+    fill_table(a.tt, trig, first, cnt, nullptr);
+    a.g.num_trig = cnt;
+    a.max_chunks = (max_len_of(trig, first, cnt) + rkv::kChunk - 1) / rkv::kChunk;
+    hipError_t e = rkv::launch_score(a, cfg->dtype == RKV_DTYPE_BF16, hs);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
+  }
+  return RKV_OK;
+}
+
+rkv_status rkv_select(const rkv_config* cfg, int32_t num_seqs, const int32_t* h_seq_lens,
+                      const float* scores, int32_t score_stride, int32_t* keep, void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  std::vector<Trig> trig;
+  if ((st = collect(cfg, nullptr, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
+  if (trig.empty()) return RKV_OK;
+  if (scores == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores is NULL");
+  if (keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
+  const int32_t maxn = max_len_of(trig, 0, trig.size());
+  if (score_stride < maxn)
+    return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
+                score_stride, maxn);
+  {
+    hipError_t e = rkv::prepare_select();
+    if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
+  }
+  rkv::SelectArgs a{};
+  a.g = make_geom(cfg, nullptr, num_seqs);
+  a.scores = scores;
+  a.keep = keep;
+  a.score_stride = score_stride;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+    const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+    fill_table(a.tt, trig, first, cnt, nullptr);
+    a.g.num_trig = cnt;
+    hipError_t e = rkv::launch_select(a, max_len_of(trig, first, cnt), hs);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+  }
+  return RKV_OK;
+}
+
+rkv_status rkv_compact(const rkv_config* cfg, const rkv_cache* cache, int32_t num_seqs,
+                       int32_t* h_seq_lens, const int32_t* keep, int32_t* free_blocks,
+                       int32_t free_capacity, int32_t* h_free_counts, void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  std::vector<Trig> trig;
+  if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
+  if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
+  const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
+  // FREE_BLOCKS counts in closed form: ceil(len/bs) - ceil(budget/bs)
+  std::vector<int32_t> counts(num_seqs > 0 ? num_seqs : 0, 0), offs(trig.size(), 0);
+  long total = 0;
+  if (paged) {
+    const int bs = cfg->block_size;
+    const long kept_blocks = ((long)cfg->budget + bs - 1) / bs;
+    for (size_t i = 0; i < trig.size(); ++i) {
+      const long used = ((long)trig[i].len + bs - 1) / bs;
+      const int32_t c = (int32_t)std::max(0L, used - kept_blocks);
+      counts[trig[i].seq] = c;
+      offs[i] = (int32_t)total;
+      total += c;
+    }
+    if (total > 0 && free_blocks == nullptr) return fail(RKV_ERR_INVALID_ARG, "free_blocks is NULL");
+    if (total > free_capacity)
+      return fail(RKV_ERR_INVALID_ARG, "free_capacity %d below the %ld freed blocks", free_capacity,
+                  total);
+  }
+  if (!trig.empty() && keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
+  if (!trig.empty()) {
+    rkv::CompactArgs a{};
+    a.g = make_geom(cfg, cache, num_seqs);
+    a.k = cache->k;
+    a.v = cache->v;
+    a.bt = cache->block_table;
+    a.keep = keep;
+    a.free_blocks = paged ? free_blocks : nullptr;
+    a.row_bytes = cfg->head_dim * (cfg->dtype == RKV_DTYPE_BF16 ? 2 : 4);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+      const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+      fill_table(a.tt, trig, first, cnt, offs.data());
+      a.g.num_trig = cnt;
+      hipError_t e = rkv::launch_compact(a, hs);
+      if (e != hipSuccess) return hip_fail(e, "compact launch");
+    }
+  }
+  for (const Trig& t : trig) h_seq_lens[t.seq] = cfg->budget;
+  if (h_free_counts != nullptr)
+    for (int32_t s = 0; s < num_seqs; ++s) h_free_counts[s] = counts[s];
+  return RKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Device-side helpers and launch arguments shared by the R-KV kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rkv.h"
+
+namespace rkv {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;         // every kernel runs 4 waves per workgroup
+constexpr int kMaxTrig = 128;         // triggered sequences per launch
+constexpr int kBlockKeys = 16;        // keys per MFMA column block
+constexpr int kBlocksPerWave = 4;     // column blocks a wave scores per chunk
+constexpr int kChunk = kBlockKeys * kBlocksPerWave * (kThreads / kWave);  // 256 keys
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Triggered sequences of one launch, passed by value as a kernel argument.
+struct TrigTable {
+  int32_t seq[kMaxTrig];       // index of the sequence in the batch
+  int32_t len[kMaxTrig];       // its cache length N (>= budget + buffer)
+  int32_t free_off[kMaxTrig];  // paged: first FREE_BLOCKS entry of the sequence
+};
+
+// Cache geometry and method constants common to all kernels.
+struct Geom {
+  int32_t num_seqs, num_layers, hq, hkv, group, d, window, budget;
+  int32_t paged;               // 0 contiguous, 1 paged
+  int32_t cap;                 // contiguous slots per (l, s, h)
+  int32_t bs_shift;            // paged: log2(block_size)
+  int32_t nblk, maxblk;        // paged: pool blocks per layer, table row length
+  int32_t num_trig;            // triggered sequences in this launch
+};
+
+// Element offset of the row of token t of (layer l, sequence s, kv head h).
+__device__ __forceinline__ int64_t row_offset(const Geom& g, const int32_t* __restrict__ bt,
+                                              int l, int s, int h, int t) {
+  if (!g.paged)
+    return ((((int64_t)l * g.num_seqs + s) * g.hkv + h) * g.cap + t) * g.d;
+  const int blk = bt[(int64_t)s * g.maxblk + (t >> g.bs_shift)];
+  const int bs = 1 << g.bs_shift;
+  return ((((int64_t)l * g.nblk + blk) * g.hkv + h) * bs + (t & (bs - 1))) * g.d;
+}
+
+// Units are (triggered sequence, layer, kv head), kv head fastest.
+struct Unit {
+  int ti, s, l, h, n;
+};
+
+__device__ __forceinline__ Unit decode_unit(const Geom& g, const TrigTable& tt, int u) {
+  Unit r;
+  r.h = u % g.hkv;
+  const int lt = u / g.hkv;
+  r.l = lt % g.num_layers;
+  r.ti = lt / g.num_layers;
+  r.s = tt.seq[r.ti];
+  r.n = tt.len[r.ti];
+  return r;
+}
+
+// Row index of a unit in the [L][S][Hkv][...] score / keep arrays.
+__device__ __forceinline__ int64_t out_row(const Geom& g, const Unit& u) {
+  return ((int64_t)u.l * g.num_seqs + u.s) * g.hkv + u.h;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+}  // namespace rkv

@@ -1,0 +1,53 @@
+// Kernel argument blocks and host launchers of the R-KV kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rkv_device.h"
+
+namespace rkv {
+
+struct ScoreArgs {
+  Geom g;
+  TrigTable tt;
+  const void* k;          // keys (contiguous cache or paged pool)
+  const void* q;          // window queries [L][S][Hq][w][d]
+  const int32_t* bt;      // paged block table or nullptr
+  float* scores;          // [L][S][Hkv][score_stride]
+  float* imp;             // optional, same layout
+  float* red;             // optional, same layout
+  float* part;            // workspace: [units][max_chunks][rec] floats
+  int32_t score_stride;
+  int32_t max_chunks;     // chunks of the longest triggered sequence
+  int32_t gw;             // window rows per unit: group * window
+  int32_t rec;            // floats per chunk record: 2 * gw + d
+  float lambda;
+  float c;                // log2(e) / sqrt(d): raw dot -> log2-scaled logit
+};
+
+struct SelectArgs {
+  Geom g;
+  TrigTable tt;
+  const float* scores;
+  int32_t* keep;          // [L][S][Hkv][budget]
+  int32_t score_stride;
+};
+
+struct CompactArgs {
+  Geom g;
+  TrigTable tt;
+  void* k;
+  void* v;
+  const int32_t* bt;
+  const int32_t* keep;
+  int32_t* free_blocks;   // paged FREE_BLOCKS output or nullptr
+  int32_t row_bytes;      // d * element size
+};
+
+hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, int max_len, hipStream_t st);
+hipError_t prepare_select();   // raise the dynamic-LDS limit of the select kernel once
+hipError_t launch_compact(const CompactArgs& a, hipStream_t st);
+
+}  // namespace rkv

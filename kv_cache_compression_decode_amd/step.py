@@ -1,0 +1,50 @@
+"""One R-KV compression step over torch device tensors.
+
+Owns the buffers a batch shape needs (workspace, scores, keep list) and calls
+the three C entry points in order on one stream.  Argument marshalling only:
+the work is done by librkv.so.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import binding as B
+
+
+class RKVStep:
+    def __init__(self, cfg: B.rkv_config, num_seqs: int, max_len: int, device="cuda",
+                 keep_parts: bool = False, free_capacity: int = 0):
+        import torch
+        self.cfg = cfg
+        self.num_seqs = num_seqs
+        self.max_len = max_len
+        rows = cfg.num_layers * num_seqs * cfg.num_kv_heads
+        self.ws_bytes = max(256, B.rkv_workspace_size(cfg, num_seqs, max_len))
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.scores = torch.empty(rows * max_len, dtype=torch.float32, device=device)
+        self.importance = torch.empty_like(self.scores) if keep_parts else None
+        self.redundancy = torch.empty_like(self.scores) if keep_parts else None
+        self.keep = torch.empty(rows * cfg.budget, dtype=torch.int32, device=device)
+        self.free_capacity = free_capacity
+        self.free_blocks = (torch.empty(max(1, free_capacity), dtype=torch.int32, device=device)
+                            if free_capacity else None)
+        self.free_counts = np.zeros(num_seqs, dtype=np.int32)
+
+    def score(self, cache: B.rkv_cache, q_window, seq_lens, stream=None) -> None:
+        B.rkv_score(self.cfg, cache, q_window, self.num_seqs, seq_lens, self.scores, self.max_len,
+                    self.importance, self.redundancy, self.workspace, self.ws_bytes, stream)
+
+    def select(self, seq_lens, stream=None) -> None:
+        B.rkv_select(self.cfg, self.num_seqs, seq_lens, self.scores, self.max_len, self.keep, stream)
+
+    def compact(self, cache: B.rkv_cache, seq_lens: np.ndarray, stream=None) -> None:
+        B.rkv_compact(self.cfg, cache, self.num_seqs, seq_lens, self.keep, self.free_blocks,
+                      self.free_capacity, self.free_counts, stream)
+
+    def __call__(self, cache: B.rkv_cache, q_window, seq_lens: np.ndarray, stream=None) -> None:
+        """score, select, compact; seq_lens (int32 numpy) is updated in place."""
+        self.score(cache, q_window, seq_lens, stream)
+        self.select(seq_lens, stream)
+        self.compact(cache, seq_lens, stream)

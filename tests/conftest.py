@@ -12,3 +12,20 @@ if HERE not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workloads (minutes)")
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a GPU; on a machine without one they are skipped (they
+    never fall back to anything else).  A missing HIP library still fails."""
+    import pytest
+    try:
+        import torch
+        have_gpu = torch.cuda.is_available()
+    except Exception:  # noqa: BLE001
+        have_gpu = False
+    if have_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU on this machine")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

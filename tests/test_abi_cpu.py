@@ -1,0 +1,163 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/rkv.h declares, and rejects bad arguments before it touches
+the device (no compute call is made here)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from kv_cache_compression_decode_amd import binding as B
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkv.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define RKV_MAX_LEN (\d+)", text).group(1)) == B.RKV_MAX_LEN
+    assert int(re.search(r"#define RKV_MAX_WINDOW_ROWS (\d+)", text).group(1)) == B.RKV_MAX_WINDOW_ROWS
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(B.rkv_config) == 44
+    assert ctypes.sizeof(B.rkv_cache) == 40
+    assert B.rkv_cache.block_table.offset == 24
+
+
+def test_status_strings():
+    for s, name in [(0, "RKV_OK"), (1, "RKV_ERR_INVALID_ARG"), (2, "RKV_ERR_UNSUPPORTED"),
+                    (3, "RKV_ERR_WORKSPACE"), (4, "RKV_ERR_HIP")]:
+        assert B.rkv_status_string(s) == name
+
+
+def cfg(**kw):
+    base = dict(num_layers=32, num_q_heads=32, num_kv_heads=8, head_dim=128, budget=1024,
+                buffer=128, window=8, mix_lambda=0.1)
+    base.update(kw)
+    dtype = base.pop("dtype", "bf16")
+    layout = base.pop("layout", "contiguous")
+    bs = base.pop("block_size", 16)
+    return B.make_config(**base, dtype=dtype, layout=layout, block_size=bs)
+
+
+FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
+
+
+def cache(**kw):
+    return B.make_cache(kw.get("k", FAKE), kw.get("v", FAKE), kw.get("capacity", 2048),
+                        kw.get("num_blocks", 0), kw.get("block_table", None),
+                        kw.get("max_blocks", 0))
+
+
+def test_trigger_rule():
+    c = cfg()
+    assert B.rkv_is_triggered(c, 1151) == 0
+    assert B.rkv_is_triggered(c, 1152) == 1
+    assert B.rkv_is_triggered(c, 5000) == 1
+
+
+def test_workspace_size_formula():
+    c = cfg()
+    # one record of 2*G*w + d floats per (unit, 256-key chunk), 256-byte rounded
+    n = B.rkv_workspace_size(c, 1, 1152)
+    assert n == 1 * 32 * 8 * math.ceil(1152 / 256) * (2 * 4 * 8 + 128) * 4
+    assert B.rkv_workspace_size(c, 200, 1152) == B.rkv_workspace_size(c, 128, 1152)
+    assert B.rkv_workspace_size(cfg(head_dim=96), 1, 1152) == 0
+
+
+def expect(status, fn, *a, **kw):
+    with pytest.raises(B.RkvError) as e:
+        fn(*a, **kw)
+    assert e.value.status == status, e.value
+    assert e.value.detail
+
+
+def score(c, ca=None, lens=(1152,), q=FAKE, scores=FAKE, stride=1152, ws=FAKE * 4, wsb=1 << 30):
+    B.rkv_score(c, cache() if ca is None else ca, q, len(lens), list(lens), scores, stride,
+                None, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_dim=96), B.RKV_ERR_UNSUPPORTED),
+    (dict(num_q_heads=30), B.RKV_ERR_INVALID_ARG),
+    (dict(budget=8), B.RKV_ERR_INVALID_ARG),
+    (dict(window=0), B.RKV_ERR_INVALID_ARG),
+    (dict(buffer=0), B.RKV_ERR_INVALID_ARG),
+    (dict(mix_lambda=1.5), B.RKV_ERR_INVALID_ARG),
+    (dict(mix_lambda=-0.1), B.RKV_ERR_INVALID_ARG),
+    (dict(mix_lambda=float("nan")), B.RKV_ERR_INVALID_ARG),
+    (dict(num_layers=0), B.RKV_ERR_INVALID_ARG),
+    (dict(window=16, num_q_heads=80, num_kv_heads=8), B.RKV_ERR_UNSUPPORTED),
+    (dict(layout="paged", block_size=24), B.RKV_ERR_UNSUPPORTED),
+    (dict(budget=40000), B.RKV_ERR_UNSUPPORTED),
+])
+def test_config_rejected(bad, status):
+    expect(status, score, cfg(**bad))
+
+
+def test_argument_errors():
+    c = cfg()
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=cache(k=None))
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=cache(k=FAKE + 8))          # misaligned
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=cache(capacity=1000))       # len > capacity
+    expect(B.RKV_ERR_INVALID_ARG, score, c, q=None)
+    expect(B.RKV_ERR_INVALID_ARG, score, c, scores=None)
+    expect(B.RKV_ERR_INVALID_ARG, score, c, stride=1000)
+    expect(B.RKV_ERR_INVALID_ARG, score, c, lens=(1152, -1))
+    expect(B.RKV_ERR_UNSUPPORTED, score, c, lens=(40000,), ca=cache(capacity=50000), stride=40000)
+    expect(B.RKV_ERR_WORKSPACE, score, c, ws=None)
+    expect(B.RKV_ERR_WORKSPACE, score, c, wsb=1000)
+    expect(B.RKV_ERR_WORKSPACE, score, c, ws=FAKE * 4 + 16)               # misaligned
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_select, c, 1, [1152], None, 1152, FAKE)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_select, c, 1, [1152], FAKE, 1152, None)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_select, c, 1, [1152], FAKE, 100, FAKE)
+    lens = np.array([1152], np.int32)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, c, cache(v=None), 1, lens, FAKE)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, c, cache(), 1, lens, None)
+    assert lens[0] == 1152, "failed call changed the lengths"
+    pc = cfg(layout="paged")
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, pc, cache(num_blocks=100, max_blocks=72), 1, lens, FAKE)
+    pca = cache(num_blocks=100, block_table=FAKE, max_blocks=72)
+    # 1152 tokens -> 72 blocks, budget 1024 -> 64 blocks: 8 freed
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, pc, pca, 1, lens, FAKE, FAKE, 7)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, pc, pca, 1, lens, FAKE, None, 8)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, pc, cache(num_blocks=100, block_table=FAKE,
+                                                             max_blocks=71), 1, lens, FAKE, FAKE, 8)
+
+
+def test_nothing_triggered_is_a_no_op():
+    """Below the trigger nothing is enqueued (safe without a GPU) and lengths stay."""
+    c = cfg()
+    lens = np.array([1151, 17, 0], np.int32)
+    B.rkv_score(c, cache(), FAKE, 3, lens, FAKE, 1152, None, None, FAKE * 4, 1 << 30, None)
+    B.rkv_select(c, 3, lens, FAKE, 1152, FAKE, None)
+    counts = np.full(3, -1, np.int32)
+    B.rkv_compact(c, cache(), 3, lens, FAKE, None, 0, counts, None)
+    assert list(lens) == [1151, 17, 0]
+    assert list(counts) == [0, 0, 0]
+    B.rkv_score(c, cache(), None, 0, None, None, 0, None, None, None, 0, None)
+
+
+def test_binding_requires_inplace_lengths():
+    with pytest.raises(TypeError):
+        B.rkv_compact(cfg(), cache(), 1, [1152], FAKE)
