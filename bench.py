@@ -1,0 +1,240 @@
+"""Benchmark of the R-KV compression step on one MI355X.
+
+One step = rkv_score + rkv_select + rkv_compact over one batch (all layers,
+all triggered units), through the C ABI, inputs already resident in HBM.
+Compaction is in place, so every step gets its own pristine copy of the
+cache, prepared before the timed region.
+
+Prints one JSON line.  Defaults: the Llama-8B-shaped single-sequence
+workload (32 layers, 32 q / 8 kv heads, d 128, bf16, N 1152, budget 1024,
+buffer 128, window 8, lambda 0.1), 20 timed steps after 3 warm-up steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "compression steps/sec (cached tokens scored/s) at 1 GPU; % MFMA / % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "compact": ["rkv_compact.hip", "rkv_device.h"],
+    "score": ["rkv_score_impl.h", "rkv_device.h"],
+    "select": ["rkv_select.hip", "rkv_device.h"],
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=1, help="workload index (0-4)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="budget of the CPU-baseline sample (0 skips it)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="after the timed region, one 256 MiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "kv_cache_compression_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source for this workload; else None."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(spec, case, seconds: float):
+    """The oracle, as it stands, on this host's cores: units of the same
+    workload until the time budget is spent; reported as steps/s."""
+    from oracle import rkv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    units = [(s, l, h) for s in range(spec.num_seqs) for l in range(spec.num_layers)
+             for h in range(spec.num_kv_heads)
+             if case.lens0[s] >= spec.budget + spec.buffer]
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        s, l, h = units[done % len(units)]
+        kr, vr = case.unit_rows(s, l, h)
+        O.step_unit(spec, case.q_host[l, s], kr, vr, h)
+        done += 1
+    dt = time.perf_counter() - t0
+    steps_per_s = done / dt / len(units)
+    return {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of the step's {len(units)} units (float64 numpy, explicit N x N "
+                      f"Gram), {dt:.1f} s; value = units/s / units per step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step shards by sequence / layer / kv head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import rkv_synth as syn
+    from gpu_harness import ContigCase, PagedCase, config_of
+    from kv_cache_compression_decode_amd import binding as B
+    from kv_cache_compression_decode_amd.step import RKVStep
+
+    spec = syn.config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = PagedCase(spec) if spec.layout == "paged" else ContigCase(spec)
+    cfg = config_of(spec)
+    nsteps = args.warmup + args.steps
+    lens0 = case.lens0.astype(np.int32)
+    maxn = int(lens0.max())
+    trig = lens0 >= spec.budget + spec.buffer
+    units = int(trig.sum()) * spec.num_layers * spec.num_kv_heads
+    step = RKVStep(cfg, spec.num_seqs, maxn, free_capacity=case.free_capacity)
+    stream = torch.cuda.current_stream()
+
+    # one pristine cache copy per step, prepared before timing
+    copies = [(case.k.clone(), case.v.clone()) for _ in range(nsteps)]
+    caches = []
+    for kc, vc in copies:
+        if spec.layout == "paged":
+            caches.append(B.make_cache(kc, vc, num_blocks=spec.num_blocks, block_table=case.bt_dev,
+                                       max_blocks_per_seq=case.bt.shape[1]))
+        else:
+            caches.append(B.make_cache(kc, vc, capacity=case.cap))
+    lens_per = [lens0.copy() for _ in range(nsteps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+    torch.cuda.synchronize()
+
+    def enqueue(i, stream):
+        e = ev[i]
+        e[0].record(stream)
+        step.score(caches[i], case.q, lens_per[i], stream)
+        e[1].record(stream)
+        step.select(lens_per[i], stream)
+        e[2].record(stream)
+        step.compact(caches[i], lens_per[i], stream)
+        e[3].record(stream)
+
+    def run(i):
+        enqueue(i, stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    # rows the compaction actually moves (keep[i] != i), from a warm-up step's keep lists
+    keep = step.keep.view(-1, spec.budget).cpu().numpy()
+    moved_rows = int((keep != np.arange(spec.budget)[None, :]).sum()) if units else 0
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        run(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    timed = ev[args.warmup:]
+    t_score = sum(e[0].elapsed_time(e[1]) for e in timed) / len(timed)
+    t_select = sum(e[1].elapsed_time(e[2]) for e in timed) / len(timed)
+    t_compact = sum(e[2].elapsed_time(e[3]) for e in timed) / len(timed)
+
+    if not (t_score > 0 and t_select > 0 and t_compact > 0
+            and t_score + t_select + t_compact <= ms * 1.05):
+        raise RuntimeError(f"implausible event timings ({t_score}, {t_select}, {t_compact} ms "
+                           f"vs {ms} ms per step)")
+    esz = 2 if spec.dtype == "bf16" else 4
+    row = spec.head_dim * esz
+    gw = spec.group * spec.window
+    tokens = int(sum(int(n) for n in lens0[trig])) * spec.num_layers * spec.num_kv_heads
+    # algorithmic bytes per launch (per unit: read K once, read the window
+    # queries, write S; compaction: moved rows of K and V read and written,
+    # plus the keep list)
+    score_bytes = tokens * row + units * gw * row + tokens * 4
+    select_bytes = tokens * 4 + units * spec.budget * 4
+    compact_bytes = moved_rows * row * 2 * 2 + units * spec.budget * 4 * 2
+    kern = {
+        "score": {"us": t_score * 1e3, "bytes": score_bytes},
+        "select": {"us": t_select * 1e3, "bytes": select_bytes},
+        "compact": {"us": t_compact * 1e3, "bytes": compact_bytes},
+    }
+    for k in kern.values():
+        k["GB/s"] = round(k["bytes"] / (k["us"] * 1e-6) / 1e9, 1) if k["us"] > 0 else None
+        k["us"] = round(k["us"], 2)
+    dom = max(kern, key=lambda k: kern[k]["us"])
+    achieved = kern[dom]["GB/s"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+    tb = measured_traffic(dom, spec.name)
+    if tb is not None:
+        roofline["traffic"] = tb
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(spec, case, args.cpu_seconds)
+
+    steps_per_s = 1e3 / ms
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "num_seqs": spec.num_seqs, "num_layers": spec.num_layers,
+                   "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_dim": spec.head_dim, "seq_lens": sorted(set(int(x) for x in lens0)),
+                   "budget": spec.budget, "buffer": spec.buffer, "window": spec.window,
+                   "mix_lambda": spec.mix_lambda, "layout": spec.layout,
+                   "triggered_units": units},
+        "tokens_scored_per_s": round(tokens / (ms * 1e-3), 1),
+        "roofline": roofline,
+        "kernels": kern,
+        "moved_rows": moved_rows,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

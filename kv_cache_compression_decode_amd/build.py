@@ -18,8 +18,9 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["rkv_api.hip", "rkv_score.hip", "rkv_score_bf16_d128.hip", "rkv_score_bf16_d64.hip",
-           "rkv_score_f32_d128.hip", "rkv_score_f32_d64.hip", "rkv_select.hip", "rkv_compact.hip"]
+SOURCES = ["rkv_api.hip", "rkv_score.hip", "rkv_select.hip", "rkv_compact.hip"] + [
+    f"rkv_score_{dt}_d{d}_{lay}.hip" for dt in ("bf16", "f32") for d in (64, 128)
+    for lay in ("contig", "paged")]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -48,7 +49,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(len(cmds)) as ex:
+    with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = OUT + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
