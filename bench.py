@@ -1,7 +1,9 @@
 """Benchmark of the R-KV compression step on one MI355X.
 
-One step = rkv_score + rkv_select + rkv_compact over one batch (all layers,
-all triggered units), through the C ABI, inputs already resident in HBM.
+One step = score, select and compact over one batch (all layers, all
+triggered units) through the C ABI's rkv_step (for this workload one fused
+kernel per launch; --three-calls times rkv_score + rkv_select + rkv_compact
+instead), inputs already resident in HBM.
 Compaction is in place, so every step gets its own pristine copy of the
 cache, prepared before the timed region.
 
@@ -27,6 +29,8 @@ METRIC = "compression steps/sec (cached tokens scored/s) at 1 GPU; % MFMA / % HB
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
+    "step": ["rkv_step_impl.h", "rkv_unit_impl.h", "rkv_select_impl.h", "rkv_score_impl.h",
+             "rkv_device.h"],
     "compact": ["rkv_compact.hip", "rkv_device.h"],
     "score": ["rkv_score_impl.h", "rkv_device.h"],
     "select": ["rkv_select.hip", "rkv_device.h"],
@@ -41,6 +45,8 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload index (0-4)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the CPU-baseline sample (0 skips it)")
+    p.add_argument("--three-calls", action="store_true",
+                   help="time rkv_score + rkv_select + rkv_compact instead of rkv_step")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed region, one 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -137,13 +143,18 @@ def main():
 
     def enqueue(i, stream):
         e = ev[i]
-        e[0].record(stream)
-        step.score(caches[i], case.q, lens_per[i], stream)
-        e[1].record(stream)
-        step.select(lens_per[i], stream)
-        e[2].record(stream)
-        step.compact(caches[i], lens_per[i], stream)
-        e[3].record(stream)
+        if args.three_calls:
+            e[0].record(stream)
+            step.score(caches[i], case.q, lens_per[i], stream)
+            e[1].record(stream)
+            step.select(lens_per[i], stream)
+            e[2].record(stream)
+            step.compact(caches[i], lens_per[i], stream)
+            e[3].record(stream)
+        else:
+            e[0].record(stream)
+            step.fused(caches[i], case.q, lens_per[i], stream)
+            e[1].record(stream)
 
     def run(i):
         enqueue(i, stream)
@@ -169,31 +180,36 @@ def main():
 
     ms = (t1 - t0) * 1e3 / args.steps
     timed = ev[args.warmup:]
-    t_score = sum(e[0].elapsed_time(e[1]) for e in timed) / len(timed)
-    t_select = sum(e[1].elapsed_time(e[2]) for e in timed) / len(timed)
-    t_compact = sum(e[2].elapsed_time(e[3]) for e in timed) / len(timed)
 
-    if not (t_score > 0 and t_select > 0 and t_compact > 0
-            and t_score + t_select + t_compact <= ms * 1.05):
-        raise RuntimeError(f"implausible event timings ({t_score}, {t_select}, {t_compact} ms "
-                           f"vs {ms} ms per step)")
+    def avg_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in timed) / len(timed)
+
     esz = 2 if spec.dtype == "bf16" else 4
     row = spec.head_dim * esz
     gw = spec.group * spec.window
     tokens = int(sum(int(n) for n in lens0[trig])) * spec.num_layers * spec.num_kv_heads
-    # algorithmic bytes per launch (per unit: read K once, read the window
-    # queries, write S; compaction: moved rows of K and V read and written,
-    # plus the keep list)
-    score_bytes = tokens * row + units * gw * row + tokens * 4
+    # algorithmic bytes per launch, per unit: read K once, read the window
+    # queries, write S and the keep list; compaction: moved rows (keep[i] != i)
+    # of K and V, each read and written once
+    q_bytes = units * gw * row
+    score_bytes = tokens * row + q_bytes + tokens * 4
     select_bytes = tokens * 4 + units * spec.budget * 4
     compact_bytes = moved_rows * row * 2 * 2 + units * spec.budget * 4 * 2
-    kern = {
-        "score": {"us": t_score * 1e3, "bytes": score_bytes},
-        "select": {"us": t_select * 1e3, "bytes": select_bytes},
-        "compact": {"us": t_compact * 1e3, "bytes": compact_bytes},
-    }
+    if args.three_calls:
+        kern = {"score": {"us": avg_ms(0, 1) * 1e3, "bytes": score_bytes},
+                "select": {"us": avg_ms(1, 2) * 1e3, "bytes": select_bytes},
+                "compact": {"us": avg_ms(2, 3) * 1e3, "bytes": compact_bytes}}
+    else:
+        # the fused kernel holds the keys on chip: keys read once, moved key rows
+        # written from registers, moved value rows read and written
+        step_bytes = (tokens * row + q_bytes + tokens * 4 + units * spec.budget * 4
+                      + moved_rows * row + moved_rows * row * 2)
+        kern = {"step": {"us": avg_ms(0, 1) * 1e3, "bytes": step_bytes}}
+    total_us = sum(k["us"] for k in kern.values())
+    if not (all(k["us"] > 0 for k in kern.values()) and total_us <= ms * 1e3 * 1.05):
+        raise RuntimeError(f"implausible event timings {kern} vs {ms} ms per step")
     for k in kern.values():
-        k["GB/s"] = round(k["bytes"] / (k["us"] * 1e-6) / 1e9, 1) if k["us"] > 0 else None
+        k["GB/s"] = round(k["bytes"] / (k["us"] * 1e-6) / 1e9, 1)
         k["us"] = round(k["us"], 2)
     dom = max(kern, key=lambda k: kern[k]["us"])
     achieved = kern[dom]["GB/s"]
@@ -228,6 +244,7 @@ def main():
                    "mix_lambda": spec.mix_lambda, "layout": spec.layout,
                    "triggered_units": units},
         "tokens_scored_per_s": round(tokens / (ms * 1e-3), 1),
+        "entry": "rkv_score+rkv_select+rkv_compact" if args.three_calls else "rkv_step",
         "roofline": roofline,
         "kernels": kern,
         "moved_rows": moved_rows,

@@ -165,6 +165,24 @@ rkv_status rkv_compact(const rkv_config *cfg, const rkv_cache *cache, int32_t nu
                        int32_t *free_blocks, int32_t free_capacity,
                        int32_t *h_free_counts, void *stream);
 
+/* The whole step in one call: the outputs of rkv_score (scores only),
+ * rkv_select and rkv_compact, with the same arguments and the same results
+ * bit for bit.  For bf16 units of up to 1280 keys (head_dim 128; 2560 at 64)
+ * with num_q_heads / num_kv_heads * window <= 78, one kernel per launch
+ * scores, selects and compacts each unit, keeping its keys on chip so the
+ * keys are read from HBM once; other launches run the three kernels in
+ * order (R-KV project page, "How R-KV decides what to drop": the step runs
+ * on the critical path, which is why it is fused where it fits).
+ *   h_seq_lens  host, in/out (triggered sequences become `budget` long)
+ *   workspace   as for rkv_score; only launches that cannot run fused use it
+ *               (NULL is accepted when every launch runs fused)
+ * Errors: the union of those of the three calls. */
+rkv_status rkv_step(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
+                    int32_t num_seqs, int32_t *h_seq_lens,
+                    float *scores, int32_t score_stride, int32_t *keep,
+                    int32_t *free_blocks, int32_t free_capacity, int32_t *h_free_counts,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,6 @@ runs the three calls on torch device tensors.
 """
 from . import binding  # noqa: F401
 from .binding import (RkvError, make_cache, make_config, rkv_compact, rkv_is_triggered,  # noqa: F401
-                      rkv_last_error, rkv_score, rkv_select, rkv_status_string,
+                      rkv_last_error, rkv_score, rkv_select, rkv_status_string, rkv_step,
                       rkv_workspace_size)
 from .step import RKVStep  # noqa: F401

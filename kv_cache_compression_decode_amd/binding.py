@@ -32,7 +32,7 @@ RKV_MAX_WINDOW_ROWS = 142
 
 # Every function declared in include/rkv.h.
 EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_workspace_size",
-           "rkv_score", "rkv_select", "rkv_compact")
+           "rkv_score", "rkv_select", "rkv_compact", "rkv_step")
 
 
 class rkv_config(ctypes.Structure):
@@ -85,6 +85,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rkv_compact.argtypes = [P(rkv_config), P(rkv_cache), c_int32, P(c_int32), c_void_p,
                                 c_void_p, c_int32, P(c_int32), c_void_p]
     lib.rkv_compact.restype = c_int32
+    lib.rkv_step.argtypes = [P(rkv_config), P(rkv_cache), c_void_p, c_int32, P(c_int32), c_void_p,
+                             c_int32, c_void_p, c_void_p, c_int32, P(c_int32), c_void_p, c_size_t,
+                             c_void_p]
+    lib.rkv_step.restype = c_int32
     _lib = lib
     return lib
 
@@ -179,6 +183,22 @@ def rkv_compact(cfg, cache, num_seqs, seq_lens: np.ndarray, keep, free_blocks=No
     _check(load().rkv_compact(ctypes.byref(cfg), ctypes.byref(cache), num_seqs, _i32p(seq_lens),
                               _ptr(keep), _ptr(free_blocks), free_capacity, _i32p(free_counts),
                               _stream(stream)))
+
+
+def rkv_step(cfg, cache, q_window, num_seqs, seq_lens: np.ndarray, scores, score_stride, keep,
+             free_blocks=None, free_capacity=0, free_counts: Optional[np.ndarray] = None,
+             workspace=None, workspace_bytes=0, stream=None) -> None:
+    """seq_lens (C-contiguous int32 numpy) is updated in place, as by rkv_compact."""
+    if not (isinstance(seq_lens, np.ndarray) and seq_lens.dtype == np.int32
+            and seq_lens.flags.c_contiguous):
+        raise TypeError("seq_lens must be a C-contiguous int32 numpy array (updated in place)")
+    if free_counts is not None and not (free_counts.dtype == np.int32
+                                        and free_counts.flags.c_contiguous):
+        raise TypeError("free_counts must be a C-contiguous int32 numpy array")
+    _check(load().rkv_step(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q_window), num_seqs,
+                           _i32p(seq_lens), _ptr(scores), score_stride, _ptr(keep),
+                           _ptr(free_blocks), free_capacity, _i32p(free_counts),
+                           _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------ helpers

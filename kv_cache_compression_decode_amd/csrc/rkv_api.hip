@@ -167,6 +167,50 @@ size_t ws_bytes_for(const rkv_config* c, long seqs, long max_len) {
   return (bytes + 255) & ~(size_t)255;
 }
 
+rkv::ScoreArgs make_score_args(const rkv_config* cfg, const rkv_cache* cache, const void* q,
+                               int32_t num_seqs, float* scores, int32_t score_stride,
+                               float* imp, float* red, void* workspace) {
+  rkv::ScoreArgs a{};
+  a.g = make_geom(cfg, cache, num_seqs);
+  a.k = cache->k;
+  a.q = q;
+  a.bt = cache->block_table;
+  a.scores = scores;
+  a.imp = imp;
+  a.red = red;
+  a.part = static_cast<float*>(workspace);
+  a.score_stride = score_stride;
+  a.gw = a.g.group * cfg->window;
+  a.rec = (int32_t)record_floats(cfg);
+  a.lambda = cfg->mix_lambda;
+  a.c = (float)(1.4426950408889634 / sqrt((double)cfg->head_dim));
+  return a;
+}
+
+// FREE_BLOCKS counts (closed form) and per-triggered-sequence offsets.
+rkv_status free_block_plan(const rkv_config* cfg, int32_t num_seqs, const std::vector<Trig>& trig,
+                           int32_t* free_blocks, int32_t free_capacity,
+                           std::vector<int32_t>& counts, std::vector<int32_t>& offs) {
+  counts.assign(num_seqs > 0 ? num_seqs : 0, 0);
+  offs.assign(trig.size(), 0);
+  if (cfg->layout != RKV_LAYOUT_PAGED) return RKV_OK;
+  const int bs = cfg->block_size;
+  const long kept_blocks = ((long)cfg->budget + bs - 1) / bs;
+  long total = 0;
+  for (size_t i = 0; i < trig.size(); ++i) {
+    const long used = ((long)trig[i].len + bs - 1) / bs;
+    const int32_t c = (int32_t)std::max(0L, used - kept_blocks);
+    counts[trig[i].seq] = c;
+    offs[i] = (int32_t)total;
+    total += c;
+  }
+  if (total > 0 && free_blocks == nullptr) return fail(RKV_ERR_INVALID_ARG, "free_blocks is NULL");
+  if (total > free_capacity)
+    return fail(RKV_ERR_INVALID_ARG, "free_capacity %d below the %ld freed blocks", free_capacity,
+                total);
+  return RKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,26 +266,15 @@ rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* 
       return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   }
 
-  rkv::ScoreArgs a{};
-  a.g = make_geom(cfg, cache, num_seqs);
-  a.k = cache->k;
-  a.q = q_window;
-  a.bt = cache->block_table;
-  a.scores = scores;
-  a.imp = importance;
-  a.red = redundancy;
-  a.part = static_cast<float*>(workspace);
-  a.score_stride = score_stride;
-  a.gw = a.g.group * cfg->window;
-  a.rec = (int32_t)record_floats(cfg);
-  a.lambda = cfg->mix_lambda;
-  a.c = (float)(1.4426950408889634 / sqrt((double)cfg->head_dim));
+  rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
+                                     importance, redundancy, workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
     const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
     fill_table(a.tt, trig, first, cnt, nullptr);
     a.g.num_trig = cnt;
-    a.max_chunks = (max_len_of(trig, first, cnt) + rkv::kChunk - 1) / rkv::kChunk;
+    a.max_len = max_len_of(trig, first, cnt);
+    a.max_chunks = (a.max_len + rkv::kChunk - 1) / rkv::kChunk;
     hipError_t e = rkv::launch_score(a, cfg->dtype == RKV_DTYPE_BF16, hs);
     if (e != hipSuccess) return hip_fail(e, "score launch");
   }
@@ -292,24 +325,9 @@ rkv_status rkv_compact(const rkv_config* cfg, const rkv_cache* cache, int32_t nu
   if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
   if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
   const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
-  // FREE_BLOCKS counts in closed form: ceil(len/bs) - ceil(budget/bs)
-  std::vector<int32_t> counts(num_seqs > 0 ? num_seqs : 0, 0), offs(trig.size(), 0);
-  long total = 0;
-  if (paged) {
-    const int bs = cfg->block_size;
-    const long kept_blocks = ((long)cfg->budget + bs - 1) / bs;
-    for (size_t i = 0; i < trig.size(); ++i) {
-      const long used = ((long)trig[i].len + bs - 1) / bs;
-      const int32_t c = (int32_t)std::max(0L, used - kept_blocks);
-      counts[trig[i].seq] = c;
-      offs[i] = (int32_t)total;
-      total += c;
-    }
-    if (total > 0 && free_blocks == nullptr) return fail(RKV_ERR_INVALID_ARG, "free_blocks is NULL");
-    if (total > free_capacity)
-      return fail(RKV_ERR_INVALID_ARG, "free_capacity %d below the %ld freed blocks", free_capacity,
-                  total);
-  }
+  std::vector<int32_t> counts, offs;
+  if ((st = free_block_plan(cfg, num_seqs, trig, free_blocks, free_capacity, counts, offs)) != RKV_OK)
+    return st;
   if (!trig.empty() && keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
   if (!trig.empty()) {
     rkv::CompactArgs a{};
@@ -326,6 +344,96 @@ rkv_status rkv_compact(const rkv_config* cfg, const rkv_cache* cache, int32_t nu
       fill_table(a.tt, trig, first, cnt, offs.data());
       a.g.num_trig = cnt;
       hipError_t e = rkv::launch_compact(a, hs);
+      if (e != hipSuccess) return hip_fail(e, "compact launch");
+    }
+  }
+  for (const Trig& t : trig) h_seq_lens[t.seq] = cfg->budget;
+  if (h_free_counts != nullptr)
+    for (int32_t s = 0; s < num_seqs; ++s) h_free_counts[s] = counts[s];
+  return RKV_OK;
+}
+
+rkv_status rkv_step(const rkv_config* cfg, const rkv_cache* cache, const void* q_window,
+                    int32_t num_seqs, int32_t* h_seq_lens, float* scores, int32_t score_stride,
+                    int32_t* keep, int32_t* free_blocks, int32_t free_capacity,
+                    int32_t* h_free_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  std::vector<Trig> trig;
+  if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
+  if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
+  std::vector<int32_t> counts, offs;
+  if ((st = free_block_plan(cfg, num_seqs, trig, free_blocks, free_capacity, counts, offs)) != RKV_OK)
+    return st;
+  const bool bf16 = cfg->dtype == RKV_DTYPE_BF16;
+  const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
+  if (!trig.empty()) {
+    if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
+    if (!aligned16(q_window)) return fail(RKV_ERR_INVALID_ARG, "q_window must be 16-byte aligned");
+    if (scores == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores is NULL");
+    if (keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
+    const int32_t maxn = max_len_of(trig, 0, trig.size());
+    if (score_stride < maxn)
+      return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
+                  score_stride, maxn);
+    rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
+                                       nullptr, nullptr, workspace);
+    // launches that cannot run fused need the scoring workspace: check them all first
+    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+      const size_t cnt = std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+      a.max_len = max_len_of(trig, first, cnt);
+      if (rkv::step_fusable(a, bf16)) continue;
+      if (workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      const size_t need = ws_bytes_for(cfg, (long)cnt, a.max_len);
+      if (workspace_bytes < need)
+        return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    }
+    {
+      const hipError_t e = rkv::prepare_select();
+      if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+      const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+      fill_table(a.tt, trig, first, cnt, offs.data());
+      a.g.num_trig = cnt;
+      a.max_len = max_len_of(trig, first, cnt);
+      a.max_chunks = (a.max_len + rkv::kChunk - 1) / rkv::kChunk;
+      hipError_t e;
+      if (rkv::step_fusable(a, bf16)) {
+        rkv::StepArgs sa{};
+        sa.s = a;
+        sa.k = cache->k;
+        sa.v = cache->v;
+        sa.keep = keep;
+        sa.free_blocks = paged ? free_blocks : nullptr;
+        e = rkv::launch_step(sa, hs);
+        if (e != hipSuccess) return hip_fail(e, "step launch");
+        continue;
+      }
+      e = rkv::launch_score(a, bf16, hs);
+      if (e != hipSuccess) return hip_fail(e, "score launch");
+      rkv::SelectArgs sl{};
+      sl.g = a.g;
+      sl.tt = a.tt;
+      sl.scores = scores;
+      sl.keep = keep;
+      sl.score_stride = score_stride;
+      e = rkv::launch_select(sl, a.max_len, hs);
+      if (e != hipSuccess) return hip_fail(e, "select launch");
+      rkv::CompactArgs ca{};
+      ca.g = a.g;
+      ca.tt = a.tt;
+      ca.k = cache->k;
+      ca.v = cache->v;
+      ca.bt = cache->block_table;
+      ca.keep = keep;
+      ca.free_blocks = paged ? free_blocks : nullptr;
+      ca.row_bytes = cfg->head_dim * (bf16 ? 2 : 4);
+      e = rkv::launch_compact(ca, hs);
       if (e != hipSuccess) return hip_fail(e, "compact launch");
     }
   }

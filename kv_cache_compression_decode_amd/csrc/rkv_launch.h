@@ -20,6 +20,7 @@ struct ScoreArgs {
   float* part;            // workspace: [units][max_chunks][rec] floats
   int32_t score_stride;
   int32_t max_chunks;     // chunks of the longest triggered sequence
+  int32_t max_len;        // longest triggered sequence of this launch
   int32_t gw;             // window rows per unit: group * window
   int32_t rec;            // floats per chunk record: 2 * gw + d
   float lambda;
@@ -45,7 +46,20 @@ struct CompactArgs {
   int32_t row_bytes;      // d * element size
 };
 
+// The fused step (score + select + compact in one kernel) for units that
+// fit the single-pass scoring.
+struct StepArgs {
+  ScoreArgs s;            // scoring arguments (keys, queries, scores, lambda, ...)
+  void* k;                // keys, written by the compaction
+  void* v;                // values
+  int32_t* keep;          // [L][S][Hkv][budget]
+  int32_t* free_blocks;   // paged FREE_BLOCKS output or nullptr
+};
+
 hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st);
+// true if launch_step can run this launch's units (else use the three kernels)
+bool step_fusable(const ScoreArgs& a, bool bf16);
+hipError_t launch_step(const StepArgs& a, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int max_len, hipStream_t st);
 hipError_t prepare_select();   // raise the dynamic-LDS limit of the select kernel once
 hipError_t launch_compact(const CompactArgs& a, hipStream_t st);

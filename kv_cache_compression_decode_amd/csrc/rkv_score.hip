@@ -1,8 +1,24 @@
-// Host launcher of the scoring pass (kernels in rkv_score_impl.h, one
-// translation unit per cache dtype, head_dim and layout).
-#include "rkv_score_impl.h"
+// Host launcher of the scoring pass: the single-pass kernel of
+// rkv_unit_impl.h for bf16 units that fit on chip, else the two kernels of
+// rkv_score_impl.h (one translation unit per cache dtype, head_dim, layout).
+#include "rkv_step_impl.h"
 
 namespace rkv {
+
+hipError_t dispatch_unit_bf16_d64_contig(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_unit_bf16_d64_paged(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_unit_bf16_d128_contig(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_unit_bf16_d128_paged(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_step_bf16_d64_contig(const StepArgs&, int, int, hipStream_t);
+hipError_t dispatch_step_bf16_d64_paged(const StepArgs&, int, int, hipStream_t);
+hipError_t dispatch_step_bf16_d128_contig(const StepArgs&, int, int, hipStream_t);
+hipError_t dispatch_step_bf16_d128_paged(const StepArgs&, int, int, hipStream_t);
+
+bool score_single_pass(const ScoreArgs& a, bool bf16, int max_len) {
+  const int rt2 = (a.gw + 2 + 15) / 16;
+  const int nmax = a.g.d == 64 ? UnitShape<64>::NMAX : UnitShape<128>::NMAX;
+  return bf16 && rt2 <= kUnitMaxRowTiles && max_len <= nmax;
+}
 
 hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st) {
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
@@ -10,6 +26,13 @@ hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   const int rt1 = (a.gw + 15) / 16;
   const int rt2 = (a.gw + 2 + 15) / 16;
+  if (score_single_pass(a, bf16, a.max_len)) {
+    if (a.g.d == 64)
+      return a.g.paged ? dispatch_unit_bf16_d64_paged(a, units, rt2, st)
+                       : dispatch_unit_bf16_d64_contig(a, units, rt2, st);
+    return a.g.paged ? dispatch_unit_bf16_d128_paged(a, units, rt2, st)
+                     : dispatch_unit_bf16_d128_contig(a, units, rt2, st);
+  }
 #define RKV_PICK(DT, D)                                                              \
   return a.g.paged ? dispatch_score_##DT##_d##D##_paged(a, grid, rt1, rt2, st)       \
                    : dispatch_score_##DT##_d##D##_contig(a, grid, rt1, rt2, st)
@@ -20,6 +43,19 @@ hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st) {
   if (a.g.d == 64) RKV_PICK(f32, 64);
   RKV_PICK(f32, 128);
 #undef RKV_PICK
+}
+
+bool step_fusable(const ScoreArgs& a, bool bf16) { return score_single_pass(a, bf16, a.max_len); }
+
+hipError_t launch_step(const StepArgs& a, hipStream_t st) {
+  const int units = a.s.g.num_trig * a.s.g.num_layers * a.s.g.hkv;
+  if (units == 0) return hipSuccess;
+  const int rt2 = (a.s.gw + 2 + 15) / 16;
+  if (a.s.g.d == 64)
+    return a.s.g.paged ? dispatch_step_bf16_d64_paged(a, units, rt2, st)
+                       : dispatch_step_bf16_d64_contig(a, units, rt2, st);
+  return a.s.g.paged ? dispatch_step_bf16_d128_paged(a, units, rt2, st)
+                     : dispatch_step_bf16_d128_contig(a, units, rt2, st);
 }
 
 }  // namespace rkv

@@ -1,9 +1,15 @@
 // Scoring kernels instantiated for bf16 caches, head_dim 128, paged layout.
-#include "rkv_score_impl.h"
+#include "rkv_step_impl.h"
 
 namespace rkv {
 hipError_t dispatch_score_bf16_d128_paged(const ScoreArgs& a, int grid, int rt1, int rt2,
                                      hipStream_t st) {
   return dispatch_score_layout<true, true, 128>(a, grid, rt1, rt2, st);
+}
+hipError_t dispatch_unit_bf16_d128_paged(const ScoreArgs& a, int units, int rt2, hipStream_t st) {
+  return dispatch_unit<true, 128>(a, units, rt2, st);
+}
+hipError_t dispatch_step_bf16_d128_paged(const StepArgs& a, int units, int rt2, hipStream_t st) {
+  return dispatch_step<true, 128>(a, units, rt2, st);
 }
 }  // namespace rkv

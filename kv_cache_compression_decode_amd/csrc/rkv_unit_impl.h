@@ -1,0 +1,304 @@
+// Single-pass scoring for units of up to 16 * 16 * NBW keys (1280 at
+// head_dim 128): one 1024-thread workgroup per unit keeps all of the unit's
+// keys in registers, so the keys are read from HBM once (the two-kernel
+// path in rkv_score_impl.h reads them twice).  Same quantities as that path
+// (R-KV project page on hysenlabs.com, "How R-KV decides what to drop";
+// hotdry blog post, R-KV section):
+//   I_j = (1/(G w)) sum_r exp(y_rj - m_r) / Z_r,  R_j = (khat_j . sum khat - 1)/(N - 1),
+//   S_j = lambda I_j - (1 - lambda) R_j.
+// Phases, each over the register-resident key fragments:
+//   1. 1/|k| per key and the unit's sum of khat (DPP row sums, LDS across waves)
+//   2. per window row, the max of q.k over all keys (keys x rows MFMA)
+//   3. per window row, sum of exp2(y - max)               (same product again)
+//   4. rows x keys MFMA with the sum of khat as two extra bf16 rows: first
+//      the redundancy (tiles holding the sum rows), then the importance
+//      (window tiles) and the mixed score.
+// Window-query rows live in LDS with a padded row pitch (D + 8 elements) so
+// the 16 rows a fragment read touches fall in different banks.
+#pragma once
+
+#include "rkv_score_impl.h"
+
+namespace rkv {
+
+constexpr int kUnitWaves = 16;
+constexpr int kUnitThreads = kUnitWaves * kWave;
+
+template <int D>
+struct UnitShape {
+  static constexpr int NBW = D == 128 ? 5 : 10;              // 16-key blocks per wave
+  static constexpr int NMAX = kUnitWaves * NBW * kBlockKeys;  // longest unit
+};
+
+// LDS of the single-pass scoring.
+template <int D, int RT>
+struct UnitLds {
+  static constexpr int QP = D + 8;                 // row pitch of the window rows (elements)
+  __attribute__((aligned(16))) uint16_t q[RT * 16 * QP];
+  float red_m[kUnitWaves][RT * 16];
+  float red_z[kUnitWaves][RT * 16];
+  float red_s[kUnitWaves][D];
+  float row_m[RT * 16], row_iz[RT * 16];
+  float rn[UnitShape<D>::NMAX];                    // 1/|k| per key, then R_j
+};
+
+// Loads the unit's keys into kf (blocks wave + 16 j) and scores them; calls
+// sink(key, S_j) once per key from the lane that holds it (after writing the
+// score outputs).  All kUnitThreads threads call it.
+template <bool PAGED, int D, int RT, typename Sink>
+__device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, UnitLds<D, RT>& L,
+                                           KeyFrag<true, D> (&kf)[UnitShape<D>::NBW], Sink sink) {
+  constexpr int KS = D / 32;
+  constexpr int NBW = UnitShape<D>::NBW;
+  constexpr int QP = UnitLds<D, RT>::QP;
+  uint16_t* q_lds = L.q;
+  auto& red_m = L.red_m;
+  auto& red_z = L.red_z;
+  auto& red_s = L.red_s;
+  float* row_m = L.row_m;
+  float* row_iz = L.row_iz;
+  float* rn_lds = L.rn;
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int col = lane & 15, g4 = lane >> 4;
+  const int t = threadIdx.x;
+  const int n = u.n;
+  const int gw = a.gw, rt1 = (gw + 15) >> 4;
+  // keys of blocks wave + 16 j into registers (missing keys as zeros)
+  KeyRows<PAGED> rows;
+  rows.init(a.g, a.bt, u);
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
+    const bool valid = key < n;
+    kf[j].load(a.k, valid ? rows.at(key) : 0, g4, valid);
+  }
+  // window rows into LDS; rows >= gw are zero until the sum rows are written
+  {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + q_offset(a, u);
+    for (int i = t; i < RT * 16 * (D / 8); i += kUnitThreads) {
+      const int r = i / (D / 8), c8 = i % (D / 8);
+      const uint4 v = r < gw ? *reinterpret_cast<const uint4*>(q + (int64_t)r * D + 8 * c8)
+                             : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(q_lds + r * QP + 8 * c8) = v;
+    }
+  }
+
+  // 1. 1/|k| and the sum of khat
+  float rn[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const float n2 = sum_rows(kf[j].sq_norm_part());
+    rn[j] = n2 > 0.f ? fast_rsqrt(n2) : 0.f;
+    const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
+    if (g4 == 0 && key < n) rn_lds[key] = rn[j];
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float s8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s8[e] = fmaf(rn[j], kf[j].at(ks, e), s8[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8[e] = sum_in_row(s8[e]);
+    if (col == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_s[wave][32 * ks + 8 * g4 + e] = s8[e];
+    }
+  }
+  __syncthreads();   // window rows in LDS
+
+  // 2. row max over all keys (keys x rows: lane holds keys 4*g4 + i of row col)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (rt >= rt1) continue;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j].w[ks]), qf[ks],
+                                                    c, 0, 0, 0);
+      const int kb = (wave + kUnitWaves * j) * kBlockKeys + 4 * g4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kb + i < n) mx = fmaxf(mx, c[i]);
+    }
+    mx = xmax32(xmax16(mx));
+    if (g4 == 0) red_m[wave][rt * 16 + col] = mx;
+  }
+  __syncthreads();
+  if (t < RT * 16) {
+    float mm = -INFINITY;
+    if (t < gw) {
+#pragma unroll
+      for (int w = 0; w < kUnitWaves; ++w) mm = fmaxf(mm, red_m[w][t]);
+    }
+    row_m[t] = t < gw ? mm * a.c : INFINITY;   // log2 units; other rows add nothing
+  }
+  __syncthreads();
+
+  // 3. row sums of exp2(y - max)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (rt >= rt1) continue;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
+    const float off = -row_m[rt * 16 + col];
+    float zz = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j].w[ks]), qf[ks],
+                                                    c, 0, 0, 0);
+      const int kb = (wave + kUnitWaves * j) * kBlockKeys + 4 * g4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kb + i < n) zz += fast_exp2(fmaf(c[i], a.c, off));
+    }
+    zz = sum_rows(zz);
+    if (g4 == 0) red_z[wave][rt * 16 + col] = zz;
+  }
+  __syncthreads();
+  if (t < RT * 16) {
+    float zz = 0.f;
+    if (t < gw) {
+#pragma unroll
+      for (int w = 0; w < kUnitWaves; ++w) zz += red_z[w][t];
+    }
+    row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
+  }
+  if (t < D) {   // sum of khat, split into the two bf16 rows gw and gw + 1
+    float sv = 0.f;
+#pragma unroll
+    for (int w = 0; w < kUnitWaves; ++w) sv += red_s[w][t];
+    const uint32_t hi = f2bf_bits(sv);
+    q_lds[gw * QP + t] = (uint16_t)hi;
+    q_lds[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
+  }
+  __syncthreads();
+
+  // 4. rows x keys (lane holds rows 4*g4 + i of key col).
+  // 4a: the tile(s) holding the sum rows give khat . sum khat, hence the
+  // redundancy, which replaces 1/|k| in LDS.
+  const int st0 = gw >> 4, st1 = (gw + 1) >> 4;
+  const float inv_nm1 = 1.f / (float)(n - 1);
+  {
+    float sd[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) sd[j] = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (rt != st0 && rt != st1) continue;
+      bf16x8 qf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], __builtin_bit_cast(bf16x8, kf[j].w[ks]),
+                                                      c, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * g4 + i;
+          if (r == gw || r == gw + 1) sd[j] += c[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const float sdj = sum_rows(sd[j]);
+      const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
+      if (g4 == 0 && key < n) {
+        const float rk = rn_lds[key];
+        rn_lds[key] = rk > 0.f ? (sdj * rk - 1.f) * inv_nm1 : 0.f;   // now R_j
+      }
+    }
+  }
+  // 4b: the window tiles give the importance; then the mixed score.
+  float ip[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) ip[j] = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (rt >= rt1) continue;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
+    float mr[4], iz[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mr[i] = row_m[rt * 16 + 4 * g4 + i];
+      iz[i] = row_iz[rt * 16 + 4 * g4 + i];
+    }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], __builtin_bit_cast(bf16x8, kf[j].w[ks]),
+                                                    c, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ip[j] = fmaf(fast_exp2(fmaf(c[i], a.c, -mr[i])), iz[i], ip[j]);
+    }
+  }
+  const int64_t orow = out_row(a.g, u) * a.score_stride;
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const float ipj = sum_rows(ip[j]);
+    const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
+    if (g4 == 0 && key < n) {
+      const float red = rn_lds[key];
+      const float sc = a.lambda * ipj - (1.f - a.lambda) * red;
+      a.scores[orow + key] = sc;
+      if (a.imp) a.imp[orow + key] = ipj;
+      if (a.red) a.red[orow + key] = red;
+      sink(key, sc);
+    }
+  }
+}
+
+template <bool PAGED, int D, int RT>
+__global__ __launch_bounds__(kUnitThreads) void score_unit_kernel(ScoreArgs a) {
+  __shared__ UnitLds<D, RT> L;
+  KeyFrag<true, D> kf[UnitShape<D>::NBW];
+  const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
+  unit_score<PAGED, D, RT>(a, u, L, kf, [](int, float) {});
+}
+
+
+template <bool PAGED, int D, int RT>
+hipError_t launch_unit_t(const ScoreArgs& a, int units, hipStream_t st) {
+  hipLaunchKernelGGL((score_unit_kernel<PAGED, D, RT>), dim3(units), dim3(kUnitThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// Window + sum rows up to 5 tiles (G * w <= 78) take the single-pass kernel.
+constexpr int kUnitMaxRowTiles = 5;
+
+template <bool PAGED, int D>
+hipError_t dispatch_unit(const ScoreArgs& a, int units, int rt2, hipStream_t st) {
+  typedef hipError_t (*Fn)(const ScoreArgs&, int, hipStream_t);
+  static const Fn fns[kUnitMaxRowTiles] = {launch_unit_t<PAGED, D, 1>, launch_unit_t<PAGED, D, 2>,
+                                           launch_unit_t<PAGED, D, 3>, launch_unit_t<PAGED, D, 4>,
+                                           launch_unit_t<PAGED, D, 5>};
+  return fns[rt2 - 1](a, units, st);
+}
+
+}  // namespace rkv

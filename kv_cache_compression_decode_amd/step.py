@@ -10,7 +10,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import binding as B
+from . import binding as B  # noqa: N812
 
 
 class RKVStep:
@@ -44,7 +44,13 @@ class RKVStep:
                       self.free_capacity, self.free_counts, stream)
 
     def __call__(self, cache: B.rkv_cache, q_window, seq_lens: np.ndarray, stream=None) -> None:
-        """score, select, compact; seq_lens (int32 numpy) is updated in place."""
+        """score, select, compact as three calls; seq_lens (int32 numpy) is updated in place."""
         self.score(cache, q_window, seq_lens, stream)
         self.select(seq_lens, stream)
         self.compact(cache, seq_lens, stream)
+
+    def fused(self, cache: B.rkv_cache, q_window, seq_lens: np.ndarray, stream=None) -> None:
+        """The same step through the single rkv_step call."""
+        B.rkv_step(self.cfg, cache, q_window, self.num_seqs, seq_lens, self.scores, self.max_len,
+                   self.keep, self.free_blocks, self.free_capacity, self.free_counts,
+                   self.workspace, self.ws_bytes, stream)
