@@ -96,6 +96,15 @@ __device__ __forceinline__ void merge_stats(float& m, float& z, float m2, float 
   m = mm;
 }
 
+// Merge (m0, z0) and (m1, z1) into (m, z); symmetric in its two pairs, so
+// partner lanes that merge each other's stats get identical results.
+__device__ __forceinline__ void merge_stats_pair(float m0, float z0, float m1, float z1, float& m,
+                                                 float& z) {
+  const float mm = fmaxf(m0, m1);
+  m = mm;
+  z = mm == -INFINITY ? 0.f : z0 * fast_exp2(m0 - mm) + z1 * fast_exp2(m1 - mm);
+}
+
 // ---------------------------------------------------------------- key operand
 template <bool BF16, int D>
 struct KeyFrag;

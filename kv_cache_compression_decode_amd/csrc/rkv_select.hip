@@ -18,7 +18,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
 
   for (int j = threadIdx.x; j < cand; j += kThreads) keys[j] = order_key(srow[j]);
   __syncthreads();
-  block_select<kThreads>(keys, cand, want, a.g.window, sh,
+  block_select<kThreads, 0>(keys, cand, want, a.g.window, sh,
                          [&](int i, int pos) { krow[i] = pos; });
 }
 

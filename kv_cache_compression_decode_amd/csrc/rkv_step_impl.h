@@ -42,11 +42,11 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   __syncthreads();
 
   int32_t* krow = sa.keep + out_row(a.g, u) * budget;
-  block_select<kUnitThreads>(keys_s, n - window, budget - window, window, ssh,
-                             [&](int i, int pos) {
-                               keep_s[i] = pos;
-                               krow[i] = pos;
-                             });
+  block_select<kUnitThreads, (NMAX + kUnitThreads - 1) / kUnitThreads>(
+      keys_s, n - window, budget - window, window, ssh, [&](int i, int pos) {
+        keep_s[i] = pos;
+        krow[i] = pos;
+      });
   __syncthreads();
   // destination slot of every token (-1: evicted); first slot that moves
   int* dest = reinterpret_cast<int*>(keys_s);

@@ -111,7 +111,9 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   }
   __syncthreads();   // window rows in LDS
 
-  // 2. row max over all keys (keys x rows: lane holds keys 4*g4 + i of row col)
+  // 2. per window row, the max of y and the sum of exp2(y - max) over all
+  // keys in one pass (keys x rows: lane holds keys 4*g4 + i of row col),
+  // rescaling the running sum whenever the running max grows
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (rt >= rt1) continue;
@@ -119,7 +121,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
-    float mx = -INFINITY;
+    float mx = -INFINITY, zz = 0.f;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -128,56 +130,46 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j].w[ks]), qf[ks],
                                                     c, 0, 0, 0);
       const int kb = (wave + kUnitWaves * j) * kBlockKeys + 4 * g4;
+      if (kb >= n) continue;   // lane-divergent; the product above is wave-wide
+      float y[4], bm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kb + i < n) mx = fmaxf(mx, c[i]);
+      for (int i = 0; i < 4; ++i) {
+        y[i] = kb + i < n ? c[i] * a.c : -INFINITY;   // log2 units
+        bm = fmaxf(bm, y[i]);
+      }
+      const float mn = fmaxf(mx, bm);                 // finite: key kb is valid
+      float zb = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zb += fast_exp2(y[i] - mn);
+      zz = fmaf(zz, fast_exp2(mx - mn), zb);
+      mx = mn;
     }
-    mx = xmax32(xmax16(mx));
-    if (g4 == 0) red_m[wave][rt * 16 + col] = mx;
+    // merge with the lanes holding the same row: l ^ 16, then l ^ 32
+    {
+      auto pm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      auto pz = __builtin_amdgcn_permlane16_swap(__float_as_uint(zz), __float_as_uint(zz), false, false);
+      const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
+      merge_stats_pair(m0, __uint_as_float(pz[0]), m1, __uint_as_float(pz[1]), mx, zz);
+    }
+    {
+      auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zz), __float_as_uint(zz), false, false);
+      const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
+      merge_stats_pair(m0, __uint_as_float(pz[0]), m1, __uint_as_float(pz[1]), mx, zz);
+    }
+    if (g4 == 0) {
+      red_m[wave][rt * 16 + col] = mx;
+      red_z[wave][rt * 16 + col] = zz;
+    }
   }
   __syncthreads();
   if (t < RT * 16) {
-    float mm = -INFINITY;
+    float mm = -INFINITY, zz = 0.f;
     if (t < gw) {
 #pragma unroll
-      for (int w = 0; w < kUnitWaves; ++w) mm = fmaxf(mm, red_m[w][t]);
+      for (int w = 0; w < kUnitWaves; ++w) merge_stats(mm, zz, red_m[w][t], red_z[w][t]);
     }
-    row_m[t] = t < gw ? mm * a.c : INFINITY;   // log2 units; other rows add nothing
-  }
-  __syncthreads();
-
-  // 3. row sums of exp2(y - max)
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    if (rt >= rt1) continue;
-    bf16x8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
-    const float off = -row_m[rt * 16 + col];
-    float zz = 0.f;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j].w[ks]), qf[ks],
-                                                    c, 0, 0, 0);
-      const int kb = (wave + kUnitWaves * j) * kBlockKeys + 4 * g4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kb + i < n) zz += fast_exp2(fmaf(c[i], a.c, off));
-    }
-    zz = sum_rows(zz);
-    if (g4 == 0) red_z[wave][rt * 16 + col] = zz;
-  }
-  __syncthreads();
-  if (t < RT * 16) {
-    float zz = 0.f;
-    if (t < gw) {
-#pragma unroll
-      for (int w = 0; w < kUnitWaves; ++w) zz += red_z[w][t];
-    }
+    row_m[t] = t < gw ? mm : INFINITY;   // log2 units; other rows add nothing
     row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
   }
   if (t < D) {   // sum of khat, split into the two bf16 rows gw and gw + 1
@@ -259,6 +251,9 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     }
   }
   const int64_t orow = out_row(a.g, u) * a.score_stride;
+  float* const s_row = a.scores + orow;
+  float* const i_row = a.imp != nullptr ? a.imp + orow : nullptr;
+  float* const r_row = a.red != nullptr ? a.red + orow : nullptr;
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const float ipj = sum_rows(ip[j]);
@@ -266,9 +261,9 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     if (g4 == 0 && key < n) {
       const float red = rn_lds[key];
       const float sc = a.lambda * ipj - (1.f - a.lambda) * red;
-      a.scores[orow + key] = sc;
-      if (a.imp) a.imp[orow + key] = ipj;
-      if (a.red) a.red[orow + key] = red;
+      s_row[key] = sc;
+      if (i_row) i_row[key] = ipj;
+      if (r_row) r_row[key] = red;
       sink(key, sc);
     }
   }
