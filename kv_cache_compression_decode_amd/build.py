@@ -52,7 +52,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = OUT + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # --no-undefined: a kernel the compiler dropped shows up here, not at load time
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp],
+         verbose)
     os.replace(tmp, OUT)
     return OUT
 

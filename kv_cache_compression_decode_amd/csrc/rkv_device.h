@@ -36,6 +36,13 @@ struct Geom {
   int32_t num_trig;            // triggered sequences in this launch
 };
 
+// Workgroup barrier that orders LDS accesses only: each wave waits for its
+// own LDS operations, not for its outstanding global loads -- in particular
+// not for loads that stream into LDS (global_load_lds) and are waited for
+// explicitly later.  The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Element offset of the row of token t of (layer l, sequence s, kv head h).
 __device__ __forceinline__ int64_t row_offset(const Geom& g, const int32_t* __restrict__ bt,
                                               int l, int s, int h, int t) {

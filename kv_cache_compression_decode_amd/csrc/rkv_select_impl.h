@@ -53,7 +53,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tot) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) tot[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int base = 0;
 #pragma unroll
   for (int w = 0; w < THREADS / kWave; ++w)
@@ -110,7 +110,7 @@ __device__ __forceinline__ void block_select(const uint32_t* keys, int cand, int
     for (int i = 0; i < MAXPER; ++i) kr[i] = lo + i < hi ? keys[lo + i] : 0u;
   }
   for (int b = tid; b < 512; b += THREADS) (&sh.hist[0][0])[b] = 0;
-  __syncthreads();
+  lds_barrier();
 
   uint32_t prefix = 0u, mask = 0u;
   int r = want;   // keys still to take at or below the prefix
@@ -128,14 +128,14 @@ __device__ __forceinline__ void block_select(const uint32_t* keys, int cand, int
         if ((kk & mask) == prefix) atomicAdd(&h[(kk >> shift) & 255u], 1);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
       find_digit(h, r, &sh.digit, &sh.above);
     } else {
       int* nxt = sh.hist[(pass + 1) & 1];
       for (int b = tid - kWave; b < 256; b += THREADS - kWave) nxt[b] = 0;
     }
-    __syncthreads();
+    lds_barrier();
     prefix |= (uint32_t)sh.digit << shift;
     mask |= 0xFFu << shift;
     r -= sh.above;

@@ -34,7 +34,11 @@ struct UnitShape {
 template <int D, int RT>
 struct UnitLds {
   static constexpr int QP = D + 8;                 // row pitch of the window rows (elements)
-  __attribute__((aligned(16))) uint16_t q[RT * 16 * QP];
+  // 16-byte pieces of the window rows, one per thread per round; the extra
+  // row only absorbs the stores of threads without a piece
+  static constexpr int QITEMS = RT * 16 * (D / 8);
+  static constexpr int QPER = (QITEMS + kUnitThreads - 1) / kUnitThreads;
+  __attribute__((aligned(16))) uint16_t q[(RT * 16 + 1) * QP];
   float red_m[kUnitWaves][RT * 16];
   float red_z[kUnitWaves][RT * 16];
   float red_s[kUnitWaves][D];
@@ -43,11 +47,14 @@ struct UnitLds {
 };
 
 // Loads the unit's keys into kf (blocks wave + 16 j) and scores them; calls
-// sink(key, S_j) once per key from the lane that holds it (after writing the
-// score outputs).  All kUnitThreads threads call it.
-template <bool PAGED, int D, int RT, typename Sink>
+// after_keys() once the keys are on chip (so that a caller can start memory
+// traffic that overlaps the arithmetic) and sink(key, S_j) once per key from
+// the lane that holds it (after writing the score outputs).  All
+// kUnitThreads threads call it.
+template <bool PAGED, int D, int RT, typename AfterKeys, typename Sink>
 __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, UnitLds<D, RT>& L,
-                                           KeyFrag<true, D> (&kf)[UnitShape<D>::NBW], Sink sink) {
+                                           KeyFrag<true, D> (&kf)[UnitShape<D>::NBW],
+                                           AfterKeys after_keys, Sink sink) {
   constexpr int KS = D / 32;
   constexpr int NBW = UnitShape<D>::NBW;
   constexpr int QP = UnitLds<D, RT>::QP;
@@ -64,24 +71,35 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   const int t = threadIdx.x;
   const int n = u.n;
   const int gw = a.gw, rt1 = (gw + 15) >> 4;
-  // keys of blocks wave + 16 j into registers (missing keys as zeros)
+  // Loads are unconditional (addresses clamped into the unit) so that no
+  // branch makes a wave wait on one load before issuing the next.  The
+  // window rows go first: writing them to LDS then waits for them only.
+  constexpr int QPER = UnitLds<D, RT>::QPER;
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + q_offset(a, u);
+  uint4 qv[QPER];
+#pragma unroll
+  for (int p = 0; p < QPER; ++p) {
+    const int i = t + p * kUnitThreads;
+    const int r = min(i / (D / 8), gw - 1), c8 = i % (D / 8);
+    qv[p] = *reinterpret_cast<const uint4*>(q + (int64_t)r * D + 8 * c8);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // window-row loads issue before the key loads
+  // keys of blocks wave + 16 j into registers; a lane past the end loads the
+  // unit's last key, which every later use masks out
   KeyRows<PAGED> rows;
   rows.init(a.g, a.bt, u);
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
-    const bool valid = key < n;
-    kf[j].load(a.k, valid ? rows.at(key) : 0, g4, valid);
+    kf[j].load(a.k, rows.at(min(key, n - 1)), g4, true);
   }
   // window rows into LDS; rows >= gw are zero until the sum rows are written
-  {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + q_offset(a, u);
-    for (int i = t; i < RT * 16 * (D / 8); i += kUnitThreads) {
-      const int r = i / (D / 8), c8 = i % (D / 8);
-      const uint4 v = r < gw ? *reinterpret_cast<const uint4*>(q + (int64_t)r * D + 8 * c8)
-                             : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(q_lds + r * QP + 8 * c8) = v;
-    }
+#pragma unroll
+  for (int p = 0; p < QPER; ++p) {
+    const int i = t + p * kUnitThreads;
+    const int r = min(i / (D / 8), RT * 16), c8 = i % (D / 8);
+    const uint4 v = r < gw ? qv[p] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(q_lds + r * QP + 8 * c8) = v;
   }
 
   // 1. 1/|k| and the sum of khat
@@ -89,8 +107,8 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const float n2 = sum_rows(kf[j].sq_norm_part());
-    rn[j] = n2 > 0.f ? fast_rsqrt(n2) : 0.f;
     const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
+    rn[j] = key < n && n2 > 0.f ? fast_rsqrt(n2) : 0.f;
     if (g4 == 0 && key < n) rn_lds[key] = rn[j];
   }
 #pragma unroll
@@ -110,6 +128,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     }
   }
   __syncthreads();   // window rows in LDS
+  after_keys();
 
   // 2. per window row, the max of y and the sum of exp2(y - max) over all
   // keys in one pass (keys x rows: lane holds keys 4*g4 + i of row col),
@@ -162,7 +181,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       red_z[wave][rt * 16 + col] = zz;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (t < RT * 16) {
     float mm = -INFINITY, zz = 0.f;
     if (t < gw) {
@@ -180,7 +199,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     q_lds[gw * QP + t] = (uint16_t)hi;
     q_lds[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
   }
-  __syncthreads();
+  lds_barrier();
 
   // 4. rows x keys (lane holds rows 4*g4 + i of key col).
   // 4a: the tile(s) holding the sum rows give khat . sum khat, hence the
@@ -274,7 +293,7 @@ __global__ __launch_bounds__(kUnitThreads) void score_unit_kernel(ScoreArgs a) {
   __shared__ UnitLds<D, RT> L;
   KeyFrag<true, D> kf[UnitShape<D>::NBW];
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
-  unit_score<PAGED, D, RT>(a, u, L, kf, [](int, float) {});
+  unit_score<PAGED, D, RT>(a, u, L, kf, [] {}, [](int, float) {});
 }
 
 
