@@ -81,6 +81,18 @@ def select_keep(scores: Sequence[float], n: int, budget: int, window: int) -> Li
     return keep
 
 
+def select_keep_shared(head_scores: Sequence[Sequence[float]], n: int, budget: int,
+                       window: int) -> List[int]:
+    """Head-shared mode: sum the heads' scores token by token, then select."""
+    total = []
+    for j in range(n):
+        t = 0.0
+        for h in range(len(head_scores)):
+            t += head_scores[h][j]
+        total.append(t)
+    return select_keep(total, n, budget, window)
+
+
 def compact(rows: Sequence[Row], keep: Sequence[int]) -> List[Row]:
     out = []
     for i in range(len(keep)):

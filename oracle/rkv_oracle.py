@@ -35,6 +35,7 @@ __all__ = [
     "decode", "is_triggered", "window_logits", "importance", "cosine_gram",
     "redundancy", "mixed_score", "score_unit", "select_keep", "compact_rows",
     "free_blocks", "unit_step", "q_group", "step_contiguous", "step_unit",
+    "shared_score", "select_keep_shared", "layer_step_shared",
 ]
 
 
@@ -128,6 +129,22 @@ def select_keep(scores: np.ndarray, n: int, budget: int, window: int) -> np.ndar
     return np.concatenate([chosen, np.arange(cand, n)]).astype(np.int64)
 
 
+def shared_score(head_scores: np.ndarray) -> np.ndarray:
+    """Head-shared mode.  [PROJ] "How R-KV decides what to drop": under tensor
+    parallelism every rank evicts the identical token set.  Reading: the KV
+    heads of one (sequence, layer) rank the tokens by the sum of their mixed
+    scores S_h (an (H, N) array -> N); the sum, not a mean, so the ranking
+    needs no division (a mean ranks identically)."""
+    hs = np.asarray(head_scores, dtype=np.float64)
+    return hs.sum(axis=0)
+
+
+def select_keep_shared(head_scores: np.ndarray, n: int, budget: int, window: int) -> np.ndarray:
+    """One keep set for all KV heads of a (sequence, layer): the per-unit
+    rule of select_keep applied to the summed scores."""
+    return select_keep(shared_score(head_scores), n, budget, window)
+
+
 def compact_rows(rows: np.ndarray, keep: np.ndarray) -> np.ndarray:
     """Slot i of the compacted cache receives row keep[i] ([PROJ]: two-phase
     compaction of the kept entries).  Plain fancy indexing."""
@@ -155,6 +172,19 @@ def unit_step(q_rows, k, k_store, v_store, budget, window, lam):
                 k_new=compact_rows(k_store, keep), v_new=compact_rows(v_store, keep))
 
 
+def layer_step_shared(q_rows_per_head, k_per_head, k_store, v_store, budget, window, lam):
+    """Head-shared mode for one (sequence, layer): I, R, S of every KV head
+    as in unit_step, one keep set from the summed S, and every head's K and
+    V compacted with it.  Arguments are per-head lists (float64 q rows and
+    keys; storage-dtype key and value rows)."""
+    heads = [score_unit(q, k, lam) for q, k in zip(q_rows_per_head, k_per_head)]
+    n = k_per_head[0].shape[0]
+    keep = select_keep_shared(np.stack([h[2] for h in heads]), n, budget, window)
+    return [dict(imp=imp, red=red, score=sc, keep=keep,
+                 k_new=compact_rows(ks, keep), v_new=compact_rows(vs, keep))
+            for (imp, red, sc), ks, vs in zip(heads, k_store, v_store)]
+
+
 def q_group(q_seq_layer: np.ndarray, h: int, group: int) -> np.ndarray:
     """Window-query rows of the query heads that share kv head h (GQA: query
     head j uses kv head j // group): (group, w, d) -> (group*w, d)."""
@@ -162,10 +192,11 @@ def q_group(q_seq_layer: np.ndarray, h: int, group: int) -> np.ndarray:
     return qg.reshape(-1, qg.shape[-1])
 
 
-def step_contiguous(spec, k, v, q, lens) -> Dict[str, object]:
+def step_contiguous(spec, k, v, q, lens, shared: bool = False) -> Dict[str, object]:
     """Whole step over contiguous caches k, v (L, S, Hkv, cap, d) and window
     queries q (L, S, Hq, w, d), all in storage dtype.  Returns per-unit results
-    of triggered sequences and the new lengths.  Meant for small cases."""
+    of triggered sequences and the new lengths.  shared: the head-shared
+    selection of layer_step_shared.  Meant for small cases."""
     group = spec.num_q_heads // spec.num_kv_heads
     out = {"units": {}, "lens": np.array(lens, dtype=np.int64).copy()}
     for s in range(spec.num_seqs):
@@ -174,7 +205,17 @@ def step_contiguous(spec, k, v, q, lens) -> Dict[str, object]:
             continue
         for l in range(spec.num_layers):
             qd = decode(q[l, s], spec.dtype)
-            for h in range(spec.num_kv_heads):
+            heads = range(spec.num_kv_heads)
+            if shared:
+                res = layer_step_shared(
+                    [q_group(qd, h, group) for h in heads],
+                    [decode(k[l, s, h, :n], spec.dtype) for h in heads],
+                    [k[l, s, h, :n] for h in heads], [v[l, s, h, :n] for h in heads],
+                    spec.budget, spec.window, spec.mix_lambda)
+                for h in heads:
+                    out["units"][(s, l, h)] = res[h]
+                continue
+            for h in heads:
                 out["units"][(s, l, h)] = unit_step(
                     q_group(qd, h, group), decode(k[l, s, h, :n], spec.dtype),
                     k[l, s, h, :n], v[l, s, h, :n], spec.budget, spec.window,

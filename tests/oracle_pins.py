@@ -69,6 +69,12 @@ def pin_golden_select(o):
         assert list(got) == ex["expect"], (ex["name"], got)
 
 
+def pin_golden_select_shared(o):
+    for ex in golden("hand_examples.json")["select_shared"]:
+        got = o.select_keep_shared(np.array(ex["scores"]), ex["n"], ex["budget"], ex["window"])
+        assert list(got) == ex["expect"], (ex["name"], got)
+
+
 def pin_golden_free_blocks(o):
     for ex in golden("hand_examples.json")["free_blocks"]:
         got = o.free_blocks(ex["bt_row"], ex["n"], ex["budget"], ex["block_size"])
@@ -309,6 +315,47 @@ def pin_brute_force_tiny_config(o, spec=None):
     _close(red, br)
     _close(s, bsc)
     assert list(o.select_keep(s, n, spec.budget, spec.window)) == bkeep
+
+
+def pin_shared_selection_special_cases(o):
+    """Head-shared selection: one KV head is the per-head rule; identical
+    heads (4 of them, so the sum is exact) select what each would alone; the
+    heads' order does not matter (integer-valued scores: exact sums); scalar
+    brute force agrees on random cases."""
+    rng = np.random.default_rng([77, 900])
+    for trial in range(20):
+        n = int(rng.integers(6, 40))
+        window = int(rng.integers(1, 4))
+        budget = int(rng.integers(window + 1, n + 1))
+        s = rng.standard_normal(n)
+        assert list(o.select_keep_shared(s[None, :], n, budget, window)) == \
+            list(o.select_keep(s, n, budget, window))
+        assert list(o.select_keep_shared(np.stack([s] * 4), n, budget, window)) == \
+            list(o.select_keep(s, n, budget, window))
+        hs = rng.integers(-20, 20, size=(3, n)).astype(np.float64)
+        ref = list(o.select_keep_shared(hs, n, budget, window))
+        assert list(o.select_keep_shared(hs[::-1].copy(), n, budget, window)) == ref
+        assert ref == brute.select_keep_shared(hs.tolist(), n, budget, window)
+        assert ref[-window:] == list(range(n - window, n))
+
+
+def pin_shared_layer_step(o):
+    """The head-shared layer step: every head's scores equal its per-head
+    unit scores, every head gets the same keep set (the rule applied to the
+    summed scores), and compaction gathers each head's own rows."""
+    rng = np.random.default_rng([77, 901])
+    heads, n, d, rows = 3, 24, 8, 4
+    qs = [rng.standard_normal((rows, d)) for _ in range(heads)]
+    ks = [rng.standard_normal((n, d)) for _ in range(heads)]
+    vs = [rng.standard_normal((n, d)) for _ in range(heads)]
+    res = o.layer_step_shared(qs, ks, ks, vs, 16, 3, 0.3)
+    per = [o.unit_step(q, k, k, v, 16, 3, 0.3) for q, k, v in zip(qs, ks, vs)]
+    total = brute.select_keep_shared([list(p["score"]) for p in per], n, 16, 3)
+    for h in range(heads):
+        _close(res[h]["score"], per[h]["score"])
+        assert list(res[h]["keep"]) == total
+        _close(res[h]["v_new"], vs[h][np.array(total)])
+        _close(res[h]["k_new"], ks[h][np.array(total)])
 
 
 def pin_page_defaults(o):

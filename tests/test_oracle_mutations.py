@@ -44,11 +44,17 @@ MUTANTS = [
      "qg = q_seq_layer[h::q_seq_layer.shape[0] // group]"),
     ("transposed Gram operand", "return khat @ khat.T", "return khat.T @ khat"),
     ("gather off by one", "return rows[np.asarray(keep)]", "return rows[np.minimum(np.asarray(keep) + 1, len(rows) - 1)]"),
+    ("shared: max over heads", "return hs.sum(axis=0)", "return hs.max(axis=0)"),
+    ("shared: first head only", "return hs.sum(axis=0)", "return hs[0]"),
+    ("shared: mean over heads", "return hs.sum(axis=0)", "return hs.mean(axis=0)"),
+    ("shared layer: per-head keep", "keep = select_keep_shared(np.stack([h[2] for h in heads]), n, budget, window)",
+     "keep = select_keep(heads[0][2], n, budget, window)"),
 ]
 
 # Mathematically neutral edits: the pins must NOT reject these (softmax is
-# invariant to a per-row or global shift).
-NEUTRAL = {"max over the wrong axis", "rows reversed before the row mean"}
+# invariant to a per-row or global shift; a mean over heads ranks as the sum).
+NEUTRAL = {"max over the wrong axis", "rows reversed before the row mean",
+           "shared: mean over heads"}
 
 
 def _mutant(old, new):
