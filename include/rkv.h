@@ -87,6 +87,14 @@ typedef struct rkv_config {
   int32_t dtype;          /* rkv_dtype of K, V and the window queries           */
   int32_t layout;         /* rkv_layout of K and V                              */
   int32_t block_size;     /* paged: tokens per block (>= 1); ignored otherwise  */
+  int32_t shared_selection; /* 0: each KV head keeps its own budget tokens.
+                               1: the KV heads of a (sequence, layer) keep one
+                               common set, ranked by the sum of their scores
+                               (head 0 + head 1 + ... in float32, in that order)
+                               -- the identical eviction the R-KV project page
+                               describes for tensor-parallel ranks ("How R-KV
+                               decides what to drop").  Scores are still per
+                               head; every head's keep row holds the same list. */
 } rkv_config;
 
 /* The KV cache the step reads and compacts (device memory, caller-owned). */
@@ -137,6 +145,9 @@ rkv_status rkv_score(const rkv_config *cfg, const rkv_cache *cache, const void *
  * keep[budget-window .. budget) = len-window .. len-1 (the window).  Candidates
  * are ranked by score descending, ties by lower position; -0.0 ranks equal to
  * +0.0.  NaN scores give an unspecified (but in-range, duplicate-free) set.
+ * With cfg->shared_selection = 1 the ranking score of a token is the float32
+ * sum of its scores over the KV heads of its (sequence, layer), and all those
+ * heads receive the same keep row.
  *   scores  device float32 (layout above), as written by rkv_score
  *   keep    device int32 (layout above)
  * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP. */
@@ -168,7 +179,8 @@ rkv_status rkv_compact(const rkv_config *cfg, const rkv_cache *cache, int32_t nu
 /* The whole step in one call: the outputs of rkv_score (scores only),
  * rkv_select and rkv_compact, with the same arguments and the same results
  * bit for bit.  For bf16 units of up to 1280 keys (head_dim 128; 2560 at 64)
- * with num_q_heads / num_kv_heads * window <= 78, one kernel per launch
+ * with num_q_heads / num_kv_heads * window <= 78 and per-head selection
+ * (shared_selection = 0), one kernel per launch
  * scores, selects and compacts each unit, keeping its keys on chip so the
  * keys are read from HBM once; other launches run the three kernels in
  * order (R-KV project page, "How R-KV decides what to drop": the step runs

@@ -39,7 +39,7 @@ class rkv_config(ctypes.Structure):
     _fields_ = [("num_layers", c_int32), ("num_q_heads", c_int32), ("num_kv_heads", c_int32),
                 ("head_dim", c_int32), ("budget", c_int32), ("buffer", c_int32),
                 ("window", c_int32), ("mix_lambda", c_float), ("dtype", c_int32),
-                ("layout", c_int32), ("block_size", c_int32)]
+                ("layout", c_int32), ("block_size", c_int32), ("shared_selection", c_int32)]
 
 
 class rkv_cache(ctypes.Structure):
@@ -204,11 +204,12 @@ def rkv_step(cfg, cache, q_window, num_seqs, seq_lens: np.ndarray, scores, score
 # ------------------------------------------------------------------ helpers
 
 def make_config(num_layers, num_q_heads, num_kv_heads, head_dim, budget, buffer, window,
-                mix_lambda, dtype="bf16", layout="contiguous", block_size=16) -> rkv_config:
+                mix_lambda, dtype="bf16", layout="contiguous", block_size=16,
+                shared_selection=False) -> rkv_config:
     return rkv_config(num_layers, num_q_heads, num_kv_heads, head_dim, budget, buffer, window,
                       mix_lambda, RKV_DTYPE_BF16 if dtype == "bf16" else RKV_DTYPE_F32,
                       RKV_LAYOUT_PAGED if layout == "paged" else RKV_LAYOUT_CONTIGUOUS,
-                      block_size)
+                      block_size, 1 if shared_selection else 0)
 
 
 def make_cache(k, v, capacity=0, num_blocks=0, block_table=None, max_blocks_per_seq=0) -> rkv_cache:

@@ -70,6 +70,8 @@ rkv_status check_config(const rkv_config* c) {
     return fail(RKV_ERR_UNSUPPORTED, "group * window = %ld exceeds %d", gw, RKV_MAX_WINDOW_ROWS);
   if (c->budget > RKV_MAX_LEN)
     return fail(RKV_ERR_UNSUPPORTED, "budget %d exceeds %d", c->budget, RKV_MAX_LEN);
+  if (c->shared_selection != 0 && c->shared_selection != 1)
+    return fail(RKV_ERR_INVALID_ARG, "shared_selection must be 0 or 1");
   return RKV_OK;
 }
 
@@ -137,6 +139,7 @@ rkv::Geom make_geom(const rkv_config* c, const rkv_cache* cache, int32_t num_seq
     g.maxblk = cache->max_blocks_per_seq;
   }
   g.bs_shift = g.paged ? ilog2_exact(c->block_size) : 0;
+  g.shared = c->shared_selection;
   return g;
 }
 

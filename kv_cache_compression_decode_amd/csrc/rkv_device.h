@@ -34,6 +34,7 @@ struct Geom {
   int32_t bs_shift;            // paged: log2(block_size)
   int32_t nblk, maxblk;        // paged: pool blocks per layer, table row length
   int32_t num_trig;            // triggered sequences in this launch
+  int32_t shared;              // 1: one keep set per (sequence, layer), from the summed scores
 };
 
 // Workgroup barrier that orders LDS accesses only: each wave waits for its

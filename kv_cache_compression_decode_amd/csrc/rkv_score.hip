@@ -45,7 +45,10 @@ hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st) {
 #undef RKV_PICK
 }
 
-bool step_fusable(const ScoreArgs& a, bool bf16) { return score_single_pass(a, bf16, a.max_len); }
+// The fused kernel selects per unit, so head-shared selection runs the three kernels.
+bool step_fusable(const ScoreArgs& a, bool bf16) {
+  return !a.g.shared && score_single_pass(a, bf16, a.max_len);
+}
 
 hipError_t launch_step(const StepArgs& a, hipStream_t st) {
   const int units = a.s.g.num_trig * a.s.g.num_layers * a.s.g.hkv;

@@ -1,6 +1,8 @@
 // Selection kernel of the R-KV compression step (rule and method in
-// rkv_select_impl.h): one 256-thread workgroup per triggered unit; the
-// unit's candidate scores are staged in LDS as order keys.
+// rkv_select_impl.h): one 256-thread workgroup per triggered unit -- or, with
+// head-shared selection, per (sequence, layer), ranking by the float32 sum of
+// the heads' scores (head 0 first) and writing the keep row of every head.
+// The candidates' order keys are staged in LDS.
 #include "rkv_launch.h"
 #include "rkv_select_impl.h"
 
@@ -10,16 +12,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   extern __shared__ uint32_t keys[];
   __shared__ SelectShared<kThreads> sh;
 
-  const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
+  const int heads = a.g.shared ? a.g.hkv : 1;   // score rows ranked together
+  const Unit u = decode_unit(a.g, a.tt, blockIdx.x * heads);   // head 0 when shared
   const int cand = u.n - a.g.window;
   const int want = a.g.budget - a.g.window;
   const float* srow = a.scores + out_row(a.g, u) * a.score_stride;
   int32_t* krow = a.keep + out_row(a.g, u) * a.g.budget;
 
-  for (int j = threadIdx.x; j < cand; j += kThreads) keys[j] = order_key(srow[j]);
+  for (int j = threadIdx.x; j < cand; j += kThreads) {
+    float sc = srow[j];
+    for (int h = 1; h < heads; ++h) sc += srow[(int64_t)h * a.score_stride + j];
+    keys[j] = order_key(sc);
+  }
   __syncthreads();
-  block_select<kThreads, 0>(keys, cand, want, a.g.window, sh,
-                         [&](int i, int pos) { krow[i] = pos; });
+  block_select<kThreads, 0>(keys, cand, want, a.g.window, sh, [&](int i, int pos) {
+    for (int h = 0; h < heads; ++h) krow[(int64_t)h * a.g.budget + i] = pos;
+  });
 }
 
 hipError_t prepare_select() {
@@ -30,7 +38,7 @@ hipError_t prepare_select() {
 }
 
 hipError_t launch_select(const SelectArgs& a, int max_len, hipStream_t st) {
-  const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
+  const int units = a.g.num_trig * a.g.num_layers * (a.g.shared ? 1 : a.g.hkv);
   if (units == 0) return hipSuccess;
   const size_t lds = (size_t)max_len * sizeof(uint32_t);
   hipLaunchKernelGGL(select_kernel, dim3(units), dim3(kThreads), lds, st, a);

@@ -26,10 +26,10 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def config_of(spec: syn.Spec) -> B.rkv_config:
+def config_of(spec: syn.Spec, shared: bool = False) -> B.rkv_config:
     return B.make_config(spec.num_layers, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                          spec.budget, spec.buffer, spec.window, spec.mix_lambda, spec.dtype,
-                         spec.layout, spec.block_size)
+                         spec.layout, spec.block_size, shared_selection=shared)
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -145,10 +145,10 @@ def make_case(spec: syn.Spec, **kw):
     return PagedCase(spec, **kw) if spec.layout == "paged" else ContigCase(spec, **kw)
 
 
-def run_step(case, keep_parts=True, sentinel=True):
+def run_step(case, keep_parts=True, sentinel=True, shared=False):
     """Run score, select, compact on the case; returns (RKVStep, lens after)."""
     spec = case.spec
-    cfg = config_of(spec)
+    cfg = config_of(spec, shared)
     maxn = int(case.lens0.max())
     step = RKVStep(cfg, spec.num_seqs, maxn, keep_parts=keep_parts,
                    free_capacity=case.free_capacity)
@@ -210,6 +210,52 @@ def check_unit(case, step, s, l, h, tag=""):
     gk, gv = case.gpu_rows(s, l, h, B_)
     assert np.array_equal(gk, O.compact_rows(krows, keep)), f"{where}: compacted K differs"
     assert np.array_equal(gv, O.compact_rows(vrows, keep)), f"{where}: compacted V differs"
+    return len(diff)
+
+
+def check_layer_shared(case, step, s, l, tag=""):
+    """Head-shared selection for one (sequence, layer): every head's scores
+    within tolerance of the oracle; one keep row shared by all heads, equal to
+    the oracle's rule applied to the float32 sum of the GPU's scores (head 0
+    first, the kernel's order) and to the float64 oracle's shared set outside
+    the threshold band; every head's compacted rows bit-exact."""
+    from oracle import rkv_oracle as O
+    spec = case.spec
+    n = int(case.lens0[s])
+    B_, w, H = spec.budget, spec.window, spec.num_kv_heads
+    where = f"{tag} layer (s={s}, l={l}) N={n}"
+    ref, rows, gsc, keeps, tols = [], [], [], [], []
+    for h in range(H):
+        krows, vrows = case.unit_rows(s, l, h)
+        o = O.step_unit(spec, case.q_host[l, s], krows, vrows, h)
+        g = unit_outputs(step, spec, s, l, h, n)
+        tol_s = TOL * np.abs(o["score"]).max()
+        err_s = np.abs(g["score"].astype(np.float64) - o["score"]).max()
+        assert err_s <= tol_s, f"{where} head {h}: score off by {err_s:.3e} (tol {tol_s:.3e})"
+        ref.append(o["score"])
+        rows.append((krows, vrows))
+        gsc.append(g["score"].astype(np.float32))
+        keeps.append(g["keep"].astype(np.int64))
+        tols.append(tol_s)
+    keep = keeps[0]
+    for h in range(1, H):
+        assert np.array_equal(keeps[h], keep), f"{where}: head {h} keeps a different set"
+    acc = gsc[0].copy()
+    for h in range(1, H):
+        acc = (acc + gsc[h]).astype(np.float32)
+    same = O.select_keep(acc.astype(np.float64), n, B_, w)
+    assert np.array_equal(keep, same), f"{where}: keep differs from the rule on the summed GPU scores"
+    total = O.shared_score(np.stack(ref))
+    diff = set(keep.tolist()) ^ set(O.select_keep_shared(np.stack(ref), n, B_, w).tolist())
+    if diff:
+        t = np.sort(total[: n - w])[::-1][B_ - w - 1]
+        band = float(np.sum(tols))
+        bad = [j for j in diff if abs(total[j] - t) > band]
+        assert not bad, f"{where}: keep differs outside the band at {bad[:5]}"
+    for h in range(H):
+        gk, gv = case.gpu_rows(s, l, h, B_)
+        assert np.array_equal(gk, O.compact_rows(rows[h][0], keep)), f"{where} head {h}: K differs"
+        assert np.array_equal(gv, O.compact_rows(rows[h][1], keep)), f"{where} head {h}: V differs"
     return len(diff)
 
 

@@ -39,7 +39,7 @@ def test_header_constants_match_binding():
 
 
 def test_struct_layouts():
-    assert ctypes.sizeof(B.rkv_config) == 44
+    assert ctypes.sizeof(B.rkv_config) == 48
     assert ctypes.sizeof(B.rkv_cache) == 40
     assert B.rkv_cache.block_table.offset == 24
 
@@ -113,6 +113,14 @@ def score(c, ca=None, lens=(1152,), q=FAKE, scores=FAKE, stride=1152, ws=FAKE * 
 ])
 def test_config_rejected(bad, status):
     expect(status, score, cfg(**bad))
+
+
+def test_shared_selection_flag_checked():
+    c = cfg()
+    c.shared_selection = 2
+    expect(B.RKV_ERR_INVALID_ARG, score, c)
+    assert B.make_config(1, 4, 1, 64, 128, 32, 8, 0.1, shared_selection=True).shared_selection == 1
+    assert cfg().shared_selection == 0
 
 
 def test_argument_errors():
