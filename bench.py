@@ -48,6 +48,8 @@ def parse():
                    help="budget of the CPU-baseline sample (0 skips it)")
     p.add_argument("--three-calls", action="store_true",
                    help="time rkv_score + rkv_select + rkv_compact instead of rkv_step")
+    p.add_argument("--shared", action="store_true",
+                   help="head-shared selection (one keep set per sequence and layer; three kernels)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed region, one 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -129,7 +131,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case = PagedCase(spec) if spec.layout == "paged" else ContigCase(spec)
-    cfg = config_of(spec)
+    cfg = config_of(spec, shared=args.shared)
     if args.steps is None:
         copy_bytes = case.k.numel() * case.k.element_size() * 2
         args.steps = int(max(5, min(100, (40 << 30) // copy_bytes - args.warmup)))
@@ -220,7 +222,7 @@ def main():
         # written from registers, moved value rows read and written
         step_bytes = (tokens * row + q_bytes + tokens * 4 + units * spec.budget * 4
                       + moved_rows * row + moved_rows * row * 2)
-        if not fused_launch(spec, lens0[trig]):
+        if args.shared or not fused_launch(spec, lens0[trig]):
             raise SystemExit(f"{spec.name}: rkv_step runs the three kernels here; "
                              "time it with --three-calls")
         kern = {"step": {"us": region_us, "bytes": step_bytes}}
@@ -264,6 +266,7 @@ def main():
                    "triggered_units": units},
         "tokens_scored_per_s": round(tokens / (ms * 1e-3), 1),
         "entry": "rkv_score+rkv_select+rkv_compact" if args.three_calls else "rkv_step",
+        "selection": "head-shared" if args.shared else "per kv head",
         "roofline": roofline,
         "kernels": kern,
         "kernel_timing": ("HIP events around each kernel" if args.three_calls else
