@@ -195,6 +195,38 @@ rkv_status rkv_step(const rkv_config *cfg, const rkv_cache *cache, const void *q
                     int32_t *free_blocks, int32_t free_capacity, int32_t *h_free_counts,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace rkv_step_device needs for num_seqs sequences of
+ * lengths up to max_len (the triggered-sequence table, plus the scoring
+ * records when the launch cannot run fused).  0 on invalid arguments. */
+size_t rkv_step_device_workspace_size(const rkv_config *cfg, int32_t num_seqs, int32_t max_len);
+
+/* rkv_step with the sequence lengths in device memory, for a step that runs
+ * inside a captured decode graph (the "in-graph decode" of the R-KV project
+ * page's SGLang port, section "How R-KV decides what to drop"): the host
+ * takes no decision that depends on the lengths, every launch has a shape
+ * fixed by (num_seqs, max_len), and the trigger is taken on the GPU.
+ * Results are those of rkv_step for the same lengths, bit for bit.
+ *   d_seq_lens    device int32 [num_seqs], in/out: triggered sequences
+ *                 (budget + buffer <= len <= max_len) become `budget` long.
+ *                 A length above max_len is left alone (not compressed).
+ *   max_len       host: upper bound of the lengths this call may compress;
+ *                 sizes the launches and the workspace.  <= RKV_MAX_LEN, and
+ *                 <= capacity (contiguous) or max_blocks_per_seq * block_size
+ *                 (paged).  score_stride >= max_len.
+ *   free_blocks   paged: as for rkv_compact; free_capacity must cover every
+ *                 sequence triggering at max_len:
+ *                 num_seqs * (ceil(max_len/bs) - ceil(budget/bs)) entries.
+ *   d_free_counts device int32 [num_seqs] or NULL: freed blocks per sequence.
+ *   workspace     device, >= rkv_step_device_workspace_size(cfg, num_seqs,
+ *                 max_len) bytes, 256-byte aligned; contents on entry ignored.
+ * Errors: those of rkv_step, checked on the host before anything is enqueued
+ * (lengths are not read by the host). */
+rkv_status rkv_step_device(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
+                           int32_t num_seqs, int32_t *d_seq_lens, int32_t max_len,
+                           float *scores, int32_t score_stride, int32_t *keep,
+                           int32_t *free_blocks, int32_t free_capacity, int32_t *d_free_counts,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,8 @@ RKV_MAX_WINDOW_ROWS = 142
 
 # Every function declared in include/rkv.h.
 EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_workspace_size",
-           "rkv_score", "rkv_select", "rkv_compact", "rkv_step")
+           "rkv_score", "rkv_select", "rkv_compact", "rkv_step",
+           "rkv_step_device_workspace_size", "rkv_step_device")
 
 
 class rkv_config(ctypes.Structure):
@@ -89,6 +90,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              c_int32, c_void_p, c_void_p, c_int32, P(c_int32), c_void_p, c_size_t,
                              c_void_p]
     lib.rkv_step.restype = c_int32
+    lib.rkv_step_device_workspace_size.argtypes = [P(rkv_config), c_int32, c_int32]
+    lib.rkv_step_device_workspace_size.restype = c_size_t
+    lib.rkv_step_device.argtypes = [P(rkv_config), P(rkv_cache), c_void_p, c_int32, c_void_p,
+                                    c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.rkv_step_device.restype = c_int32
     _lib = lib
     return lib
 
@@ -199,6 +206,22 @@ def rkv_step(cfg, cache, q_window, num_seqs, seq_lens: np.ndarray, scores, score
                            _i32p(seq_lens), _ptr(scores), score_stride, _ptr(keep),
                            _ptr(free_blocks), free_capacity, _i32p(free_counts),
                            _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def rkv_step_device_workspace_size(cfg: rkv_config, num_seqs: int, max_len: int) -> int:
+    return load().rkv_step_device_workspace_size(ctypes.byref(cfg), num_seqs, max_len)
+
+
+def rkv_step_device(cfg, cache, q_window, num_seqs, d_seq_lens, max_len, scores, score_stride,
+                    keep, free_blocks=None, free_capacity=0, d_free_counts=None, workspace=None,
+                    workspace_bytes=0, stream=None) -> None:
+    """d_seq_lens and d_free_counts are device int32 buffers (torch tensors or
+    addresses); the lengths are updated on the device."""
+    _check(load().rkv_step_device(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q_window),
+                                  num_seqs, _ptr(d_seq_lens), max_len, _ptr(scores),
+                                  score_stride, _ptr(keep), _ptr(free_blocks), free_capacity,
+                                  _ptr(d_free_counts), _ptr(workspace), workspace_bytes,
+                                  _stream(stream)))
 
 
 # ------------------------------------------------------------------ helpers

@@ -214,6 +214,25 @@ rkv_status free_block_plan(const rkv_config* cfg, int32_t num_seqs, const std::v
   return RKV_OK;
 }
 
+// Device path (rkv_step_device): the table sits at the start of the
+// workspace, the scoring records after it.
+size_t dev_table_bytes(long seqs) { return ((size_t)(1 + 3 * seqs) * 4 + 255) & ~(size_t)255; }
+
+size_t dev_records_bytes(const rkv_config* c, long seqs, long max_len) {
+  const long chunks = (max_len + rkv::kChunk - 1) / rkv::kChunk;
+  const size_t b = (size_t)seqs * c->num_layers * c->num_kv_heads * chunks * record_floats(c) * 4;
+  return (b + 255) & ~(size_t)255;
+}
+
+bool dev_fusable(const rkv_config* c, int32_t max_len) {
+  rkv::ScoreArgs a{};
+  a.g.d = c->head_dim;
+  a.g.shared = c->shared_selection;
+  a.gw = (c->num_q_heads / c->num_kv_heads) * c->window;
+  a.max_len = max_len;
+  return rkv::step_fusable(a, c->dtype == RKV_DTYPE_BF16);
+}
+
 }  // namespace
 
 extern "C" {
@@ -443,6 +462,116 @@ rkv_status rkv_step(const rkv_config* cfg, const rkv_cache* cache, const void* q
   for (const Trig& t : trig) h_seq_lens[t.seq] = cfg->budget;
   if (h_free_counts != nullptr)
     for (int32_t s = 0; s < num_seqs; ++s) h_free_counts[s] = counts[s];
+  return RKV_OK;
+}
+
+size_t rkv_step_device_workspace_size(const rkv_config* cfg, int32_t num_seqs, int32_t max_len) {
+  if (check_config(cfg) != RKV_OK || num_seqs < 0 || max_len < 0 || max_len > RKV_MAX_LEN) return 0;
+  size_t b = dev_table_bytes(num_seqs);
+  if (!dev_fusable(cfg, max_len)) b += dev_records_bytes(cfg, num_seqs, max_len);
+  return b;
+}
+
+rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const void* q_window,
+                           int32_t num_seqs, int32_t* d_seq_lens, int32_t max_len, float* scores,
+                           int32_t score_stride, int32_t* keep, int32_t* free_blocks,
+                           int32_t free_capacity, int32_t* d_free_counts, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
+  if (num_seqs < 0) return fail(RKV_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return RKV_OK;
+  if (d_seq_lens == nullptr) return fail(RKV_ERR_INVALID_ARG, "d_seq_lens is NULL");
+  if (max_len < 0) return fail(RKV_ERR_INVALID_ARG, "max_len must be >= 0");
+  if (max_len > RKV_MAX_LEN)
+    return fail(RKV_ERR_UNSUPPORTED, "max_len %d exceeds %d", max_len, RKV_MAX_LEN);
+  const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
+  const bool bf16 = cfg->dtype == RKV_DTYPE_BF16;
+  if (!paged && max_len > cache->capacity)
+    return fail(RKV_ERR_INVALID_ARG, "max_len %d exceeds capacity %d", max_len, cache->capacity);
+  if (paged && (long)max_len > (long)cache->max_blocks_per_seq * cfg->block_size)
+    return fail(RKV_ERR_INVALID_ARG, "max_len %d exceeds the block table (%d blocks)", max_len,
+                cache->max_blocks_per_seq);
+  if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
+  if (!aligned16(q_window)) return fail(RKV_ERR_INVALID_ARG, "q_window must be 16-byte aligned");
+  if (scores == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores is NULL");
+  if (keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
+  if (score_stride < max_len)
+    return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below max_len %d", score_stride, max_len);
+  if (paged) {
+    const long bs = cfg->block_size;
+    const long per = std::max(0L, (max_len + bs - 1) / bs - (cfg->budget + bs - 1) / bs);
+    const long need = per * num_seqs;
+    if (need > 0 && free_blocks == nullptr) return fail(RKV_ERR_INVALID_ARG, "free_blocks is NULL");
+    if (need > free_capacity)
+      return fail(RKV_ERR_INVALID_ARG, "free_capacity %d below the %ld entries of the worst case",
+                  free_capacity, need);
+  }
+  if (workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = rkv_step_device_workspace_size(cfg, num_seqs, max_len);
+  if (workspace_bytes < need)
+    return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  {
+    const hipError_t e = rkv::prepare_select();
+    if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
+  }
+
+  int32_t* dtab = static_cast<int32_t*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  rkv::TableArgs ta{};
+  ta.lens = d_seq_lens;
+  ta.dtab = dtab;
+  ta.free_counts = d_free_counts;
+  ta.num_seqs = num_seqs;
+  ta.budget = cfg->budget;
+  ta.trigger = cfg->budget + cfg->buffer;
+  ta.max_len = max_len;
+  ta.block_size = paged ? cfg->block_size : 0;
+  hipError_t e = rkv::launch_table(ta, hs);
+  if (e != hipSuccess) return hip_fail(e, "table launch");
+  if (max_len < (long)cfg->budget + cfg->buffer) return RKV_OK;   // nothing can trigger
+
+  float* records = reinterpret_cast<float*>(static_cast<char*>(workspace) + dev_table_bytes(num_seqs));
+  rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
+                                     nullptr, nullptr, records);
+  a.g.num_trig = num_seqs;
+  a.g.dtab = dtab;
+  a.max_len = max_len;
+  a.max_chunks = (max_len + rkv::kChunk - 1) / rkv::kChunk;
+  if (rkv::step_fusable(a, bf16)) {
+    rkv::StepArgs sa{};
+    sa.s = a;
+    sa.k = cache->k;
+    sa.v = cache->v;
+    sa.keep = keep;
+    sa.free_blocks = paged ? free_blocks : nullptr;
+    e = rkv::launch_step(sa, hs);
+    if (e != hipSuccess) return hip_fail(e, "step launch");
+    return RKV_OK;
+  }
+  e = rkv::launch_score(a, bf16, hs);
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  rkv::SelectArgs sl{};
+  sl.g = a.g;
+  sl.scores = scores;
+  sl.keep = keep;
+  sl.score_stride = score_stride;
+  e = rkv::launch_select(sl, max_len, hs);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  rkv::CompactArgs ca{};
+  ca.g = a.g;
+  ca.k = cache->k;
+  ca.v = cache->v;
+  ca.bt = cache->block_table;
+  ca.keep = keep;
+  ca.free_blocks = paged ? free_blocks : nullptr;
+  ca.row_bytes = cfg->head_dim * (bf16 ? 2 : 4);
+  e = rkv::launch_compact(ca, hs);
+  if (e != hipSuccess) return hip_fail(e, "compact launch");
   return RKV_OK;
 }
 

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int which = (blockIdx.x / PARTS) & 1;
   const int unit_id = blockIdx.x / (2 * PARTS);
   const Unit u = decode_unit(a.g, a.tt, unit_id);
+  if (u.n == 0) return;   // past the device table's count
   const int tid = threadIdx.x;
   const int budget = a.g.budget;
   const int esize = a.row_bytes / a.g.d;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   if (a.free_blocks != nullptr && which == 0 && part == 0 && u.l == 0 && u.h == 0) {
     const int bs = 1 << a.g.bs_shift;
     const int first = (budget + bs - 1) / bs, last = (u.n + bs - 1) / bs;
-    int32_t* out = a.free_blocks + a.tt.free_off[u.ti];
+    int32_t* out = a.free_blocks + free_off(a.g, a.tt, u.ti);
     for (int b = first + tid; b < last; b += kThreads)
       out[b - first] = a.bt[(int64_t)u.s * a.g.maxblk + b];
   }

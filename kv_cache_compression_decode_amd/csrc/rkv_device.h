@@ -33,8 +33,13 @@ struct Geom {
   int32_t cap;                 // contiguous slots per (l, s, h)
   int32_t bs_shift;            // paged: log2(block_size)
   int32_t nblk, maxblk;        // paged: pool blocks per layer, table row length
-  int32_t num_trig;            // triggered sequences in this launch
+  int32_t num_trig;            // triggered sequences in this launch (device table: num_seqs)
   int32_t shared;              // 1: one keep set per (sequence, layer), from the summed scores
+  // Device-resident table of triggered sequences (rkv_step_device), or null
+  // for the by-value TrigTable: [count][seq x num_seqs][len x num_seqs]
+  // [free_off x num_seqs]; launches cover num_seqs sequences and the units of
+  // table rows >= count do nothing.
+  const int32_t* dtab;
 };
 
 // Workgroup barrier that orders LDS accesses only: each wave waits for its
@@ -59,15 +64,32 @@ struct Unit {
   int ti, s, l, h, n;
 };
 
+// A unit whose table row is past the device table's count has n = 0: every
+// kernel returns before touching memory for it.
 __device__ __forceinline__ Unit decode_unit(const Geom& g, const TrigTable& tt, int u) {
   Unit r;
   r.h = u % g.hkv;
   const int lt = u / g.hkv;
   r.l = lt % g.num_layers;
   r.ti = lt / g.num_layers;
+  if (g.dtab != nullptr) {
+    if (r.ti >= g.dtab[0]) {
+      r.s = 0;
+      r.n = 0;
+      return r;
+    }
+    r.s = g.dtab[1 + r.ti];
+    r.n = g.dtab[1 + g.num_seqs + r.ti];
+    return r;
+  }
   r.s = tt.seq[r.ti];
   r.n = tt.len[r.ti];
   return r;
+}
+
+// First FREE_BLOCKS entry of triggered row ti.
+__device__ __forceinline__ int free_off(const Geom& g, const TrigTable& tt, int ti) {
+  return g.dtab != nullptr ? g.dtab[1 + 2 * g.num_seqs + ti] : tt.free_off[ti];
 }
 
 // Row index of a unit in the [L][S][Hkv][...] score / keep arrays.

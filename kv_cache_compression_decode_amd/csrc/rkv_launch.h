@@ -56,6 +56,18 @@ struct StepArgs {
   int32_t* free_blocks;   // paged FREE_BLOCKS output or nullptr
 };
 
+// Builds the device table of triggered sequences (Geom::dtab) from device
+// lengths; sets triggered lengths to the budget and writes per-sequence
+// FREE_BLOCKS counts.
+struct TableArgs {
+  int32_t* lens;          // device [num_seqs], in/out
+  int32_t* dtab;          // device [1 + 3 * num_seqs], out
+  int32_t* free_counts;   // device [num_seqs] or nullptr
+  int32_t num_seqs, budget, trigger, max_len;
+  int32_t block_size;     // paged block size; 0 for the contiguous layout
+};
+
+hipError_t launch_table(const TableArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st);
 // true if launch_step can run this launch's units (else use the three kernels)
 bool step_fusable(const ScoreArgs& a, bool bf16);

@@ -14,6 +14,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
 
   const int heads = a.g.shared ? a.g.hkv : 1;   // score rows ranked together
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x * heads);   // head 0 when shared
+  if (u.n == 0) return;   // past the device table's count
   const int cand = u.n - a.g.window;
   const int want = a.g.budget - a.g.window;
   const float* srow = a.scores + out_row(a.g, u) * a.score_stride;

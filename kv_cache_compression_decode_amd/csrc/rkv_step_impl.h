@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[SS::PRE * SS::ROWB];
 
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
+  if (u.n == 0) return;   // past the device table's count
   const int n = u.n, budget = a.g.budget, window = a.g.window;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, g4 = lane >> 4;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   if (PAGED && sa.free_blocks != nullptr && u.l == 0 && u.h == 0) {
     const int bs = 1 << a.g.bs_shift;
     const int first = (budget + bs - 1) / bs, last_blk = (n + bs - 1) / bs;
-    int32_t* out = sa.free_blocks + a.tt.free_off[u.ti];
+    int32_t* out = sa.free_blocks + free_off(a.g, a.tt, u.ti);
     for (int b = first + t; b < last_blk; b += kUnitThreads)
       out[b - first] = a.bt[(int64_t)u.s * a.g.maxblk + b];
   }

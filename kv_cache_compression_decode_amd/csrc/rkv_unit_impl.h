@@ -293,6 +293,7 @@ __global__ __launch_bounds__(kUnitThreads) void score_unit_kernel(ScoreArgs a) {
   __shared__ UnitLds<D, RT> L;
   KeyFrag<true, D> kf[UnitShape<D>::NBW];
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
+  if (u.n == 0) return;   // past the device table's count
   unit_score<PAGED, D, RT>(a, u, L, kf, [] {}, [](int, float) {});
 }
 

@@ -1,7 +1,8 @@
 """One R-KV compression step over torch device tensors.
 
 Owns the buffers a batch shape needs (workspace, scores, keep list) and calls
-the three C entry points in order on one stream.  Argument marshalling only:
+the C entry points on one stream: the three steps in order, rkv_step, or
+rkv_step_device (lengths on the device).  Argument marshalling only:
 the work is done by librkv.so.
 """
 from __future__ import annotations
@@ -48,6 +49,23 @@ class RKVStep:
         self.score(cache, q_window, seq_lens, stream)
         self.select(seq_lens, stream)
         self.compact(cache, seq_lens, stream)
+
+    def device(self, cache: B.rkv_cache, q_window, d_seq_lens, stream=None) -> None:
+        """The step through rkv_step_device: lengths in the device int32 tensor
+        d_seq_lens (updated there), self.max_len as the launch bound, freed-block
+        counts in the device tensor self.d_free_counts.  Capturable in a graph."""
+        import torch
+        if getattr(self, "dev_ws", None) is None:
+            self.dev_ws_bytes = max(256, B.rkv_step_device_workspace_size(
+                self.cfg, self.num_seqs, self.max_len))
+            self.dev_ws = torch.empty(self.dev_ws_bytes, dtype=torch.uint8,
+                                      device=self.scores.device)
+            self.d_free_counts = torch.zeros(max(1, self.num_seqs), dtype=torch.int32,
+                                             device=self.scores.device)
+        B.rkv_step_device(self.cfg, cache, q_window, self.num_seqs, d_seq_lens, self.max_len,
+                          self.scores, self.max_len, self.keep, self.free_blocks,
+                          self.free_capacity, self.d_free_counts, self.dev_ws,
+                          self.dev_ws_bytes, stream)
 
     def fused(self, cache: B.rkv_cache, q_window, seq_lens: np.ndarray, stream=None) -> None:
         """The same step through the single rkv_step call."""

@@ -145,12 +145,14 @@ def make_case(spec: syn.Spec, **kw):
     return PagedCase(spec, **kw) if spec.layout == "paged" else ContigCase(spec, **kw)
 
 
-def run_step(case, keep_parts=True, sentinel=True, shared=False):
-    """Run score, select, compact on the case; returns (RKVStep, lens after)."""
+def run_step(case, keep_parts=True, sentinel=True, shared=False, fused=False):
+    """Run score, select, compact on the case (fused: the single rkv_step
+    call, which writes no importance / redundancy); returns (RKVStep, lens
+    after)."""
     spec = case.spec
     cfg = config_of(spec, shared)
     maxn = int(case.lens0.max())
-    step = RKVStep(cfg, spec.num_seqs, maxn, keep_parts=keep_parts,
+    step = RKVStep(cfg, spec.num_seqs, maxn, keep_parts=keep_parts and not fused,
                    free_capacity=case.free_capacity)
     if sentinel:   # rows of untriggered units must stay as they are
         step.scores.fill_(float("nan"))
@@ -159,7 +161,7 @@ def run_step(case, keep_parts=True, sentinel=True, shared=False):
             step.importance.fill_(float("nan"))
             step.redundancy.fill_(float("nan"))
     lens = case.lens0.astype(np.int32).copy()
-    step(case.cache, case.q, lens)
+    (step.fused if fused else step)(case.cache, case.q, lens)
     torch.cuda.synchronize()
     return step, lens
 

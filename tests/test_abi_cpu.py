@@ -57,7 +57,8 @@ def cfg(**kw):
     dtype = base.pop("dtype", "bf16")
     layout = base.pop("layout", "contiguous")
     bs = base.pop("block_size", 16)
-    return B.make_config(**base, dtype=dtype, layout=layout, block_size=bs)
+    shared = base.pop("shared_selection", False)
+    return B.make_config(**base, dtype=dtype, layout=layout, block_size=bs, shared_selection=shared)
 
 
 FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
@@ -169,3 +170,45 @@ def test_nothing_triggered_is_a_no_op():
 def test_binding_requires_inplace_lengths():
     with pytest.raises(TypeError):
         B.rkv_compact(cfg(), cache(), 1, [1152], FAKE)
+
+
+def step_dev(c, ca=None, n=1, lens=FAKE, max_len=1152, stride=1152, keep=FAKE, fb=None, cap=0,
+             ws=FAKE * 4, wsb=1 << 30):
+    B.rkv_step_device(c, cache() if ca is None else ca, FAKE, n, lens, max_len, FAKE, stride,
+                      keep, fb, cap, None, ws, wsb, None)
+
+
+def test_step_device_workspace_size():
+    c = cfg()
+    table = (1 + 3 * 4) * 4
+    table = (table + 255) // 256 * 256
+    # fused at this shape (bf16, N <= 1280, G*w = 32): only the table
+    assert B.rkv_step_device_workspace_size(c, 4, 1152) == table
+    # not fused (N > 1280): plus one record per (unit, 256-key chunk) for every sequence
+    rec = 4 * 32 * 8 * math.ceil(2000 / 256) * (2 * 4 * 8 + 128) * 4
+    assert B.rkv_step_device_workspace_size(c, 4, 2000) == table + (rec + 255) // 256 * 256
+    # head-shared selection never runs fused
+    assert B.rkv_step_device_workspace_size(cfg(shared_selection=True), 4, 1152) > table
+    assert B.rkv_step_device_workspace_size(c, 4, 40000) == 0
+
+
+def test_step_device_argument_errors():
+    """Every argument is checked on the host before anything is enqueued."""
+    c = cfg()
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, c, lens=None)
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, c, max_len=-1)
+    expect(B.RKV_ERR_UNSUPPORTED, step_dev, c, max_len=40000, ca=cache(capacity=50000), stride=40000)
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, c, max_len=3000)                 # > capacity 2048
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, c, stride=1000)
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, c, keep=None)
+    expect(B.RKV_ERR_WORKSPACE, step_dev, c, ws=None)
+    expect(B.RKV_ERR_WORKSPACE, step_dev, c, wsb=16)
+    expect(B.RKV_ERR_WORKSPACE, step_dev, c, ws=FAKE * 4 + 16)
+    pc = cfg(layout="paged")
+    pca = cache(num_blocks=100, block_table=FAKE, max_blocks=72)
+    # worst case: 2 sequences at 1152 tokens, 8 blocks freed each
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, pc, ca=pca, n=2, fb=FAKE, cap=15)
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, pc, ca=pca, n=2, fb=None, cap=16)
+    expect(B.RKV_ERR_INVALID_ARG, step_dev, pc, ca=cache(num_blocks=100, block_table=FAKE,
+                                                          max_blocks=71), n=2, fb=FAKE, cap=16)
+    step_dev(c, n=0)   # no sequences: nothing to do, nothing enqueued

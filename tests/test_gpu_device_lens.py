@@ -1,0 +1,148 @@
+"""rkv_step_device (lengths in device memory, trigger taken on the GPU,
+launch shapes fixed by num_seqs and max_len) against rkv_step with host
+lengths, bit for bit, eagerly and captured in a HIP graph."""
+import numpy as np
+import pytest
+import torch
+
+import rkv_synth as syn
+from gpu_harness import config_of, log, make_case
+from kv_cache_compression_decode_amd.step import RKVStep
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "llama8b-1seq": (syn.config(1), False),
+    "ragged-small": (syn.config(1).with_(name="dl-r", seed=81, num_seqs=3, num_layers=2,
+                                         num_q_heads=8, num_kv_heads=2, budget=256, buffer=32,
+                                         lens=(777, 250, 300)), False),
+    "paged-bs16": (syn.config(3).with_(name="dl-p", seed=82, num_seqs=3, num_layers=2,
+                                       num_q_heads=8, num_kv_heads=2, budget=300, buffer=45,
+                                       num_blocks=400, lens=(345, 1280, 200)), False),
+    "long-2176": (syn.config(2).with_(num_seqs=2, num_layers=2, len_range=None,
+                                      lens=(2176, 2100)), False),
+    "f32-tiny": (syn.config(0), False),
+    "shared-ragged": (syn.config(1).with_(name="dl-s", seed=83, num_seqs=3, num_layers=2,
+                                          num_q_heads=8, num_kv_heads=2, budget=256, buffer=32,
+                                          lens=(777, 250, 300)), True),
+}
+
+
+def worst_free(spec, max_len):
+    if spec.layout != "paged":
+        return 0
+    bs = spec.block_size
+    per = max(0, -(-max_len // bs) - -(-spec.budget // bs))
+    return per * spec.num_seqs
+
+
+def triggered_rows(spec, lens, st):
+    out = []
+    for s in range(spec.num_seqs):
+        n = int(lens[s])
+        if n < spec.budget + spec.buffer:
+            continue
+        for l in range(spec.num_layers):
+            for h in range(spec.num_kv_heads):
+                row = (l * spec.num_seqs + s) * spec.num_kv_heads + h
+                out.append((st.scores[row * st.max_len: row * st.max_len + n].clone(),
+                            st.keep[row * spec.budget:(row + 1) * spec.budget].clone()))
+    return out
+
+
+def host_run(spec, shared, lens, max_len, free_cap):
+    case = make_case(spec)
+    st = RKVStep(config_of(spec, shared), spec.num_seqs, max_len, free_capacity=free_cap)
+    hl = np.asarray(lens, dtype=np.int32).copy()
+    st.fused(case.cache, case.q, hl)
+    torch.cuda.synchronize()
+    total = int(st.free_counts.sum())
+    fb = None if st.free_blocks is None else st.free_blocks[:total].clone()
+    return dict(rows=triggered_rows(spec, lens, st), k=case.k.clone(), v=case.v.clone(),
+                lens=hl, counts=st.free_counts.copy(), fb=fb)
+
+
+def compare(a, b, where):
+    assert len(a["rows"]) == len(b["rows"]), where
+    for (sa, ka), (sb, kb) in zip(a["rows"], b["rows"]):
+        assert torch.equal(sa, sb), f"{where}: scores differ"
+        assert torch.equal(ka, kb), f"{where}: keep differs"
+    assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"]), f"{where}: cache differs"
+    assert np.array_equal(a["lens"], b["lens"]), (where, a["lens"], b["lens"])
+    assert np.array_equal(a["counts"], b["counts"]), (where, a["counts"], b["counts"])
+    if a["fb"] is not None:
+        assert torch.equal(a["fb"], b["fb"]), f"{where}: FREE_BLOCKS differ"
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_device_lengths_equal_host_lengths(name):
+    spec, shared = CASES[name]
+    max_len = int(max(syn.seq_lens(spec)))
+    cap = worst_free(spec, max_len)
+    ref = host_run(spec, shared, syn.seq_lens(spec), max_len, cap)
+    case = make_case(spec)
+    st = RKVStep(config_of(spec, shared), spec.num_seqs, max_len, free_capacity=cap)
+    d_lens = torch.tensor(np.asarray(syn.seq_lens(spec), dtype=np.int32), device="cuda")
+    st.device(case.cache, case.q, d_lens)
+    torch.cuda.synchronize()
+    counts = st.d_free_counts[:spec.num_seqs].cpu().numpy()
+    total = int(counts.sum())
+    got = dict(rows=triggered_rows(spec, syn.seq_lens(spec), st), k=case.k.clone(), v=case.v.clone(),
+               lens=d_lens.cpu().numpy(), counts=counts,
+               fb=None if st.free_blocks is None else st.free_blocks[:total].clone())
+    compare(got, ref, name)
+    log(f"{name}: rkv_step_device equals rkv_step")
+
+
+def test_length_above_bound_left_alone():
+    """A sequence longer than max_len is not compressed (and nothing faults)."""
+    spec, _ = CASES["ragged-small"]
+    case = make_case(spec)
+    k0, v0 = case.k.clone(), case.v.clone()
+    st = RKVStep(config_of(spec), spec.num_seqs, 700)   # seq 0 has 777 > 700
+    d_lens = torch.tensor(np.asarray(syn.seq_lens(spec), dtype=np.int32), device="cuda")
+    st.device(case.cache, case.q, d_lens)
+    torch.cuda.synchronize()
+    lens = d_lens.cpu().numpy()
+    assert lens[0] == 777 and lens[1] == 250 and lens[2] == spec.budget
+    assert torch.equal(case.k[:, 0], k0[:, 0]) and torch.equal(case.v[:, 0], v0[:, 0])
+    ref = host_run(spec, False, (0, 250, 300), 700, 0)   # seq 2 alone
+    assert torch.equal(case.k[:, 2], ref["k"][:, 2]) and torch.equal(case.v[:, 2], ref["v"][:, 2])
+
+
+@pytest.mark.parametrize("name", ["ragged-small", "paged-bs16", "long-2176"])
+def test_device_step_in_graph(name):
+    """Captured once, replayed with different device lengths and fresh cache
+    contents (eager copies between replays); every replay equals rkv_step."""
+    spec, shared = CASES[name]
+    lens0 = np.asarray(syn.seq_lens(spec), dtype=np.int32)
+    max_len = int(lens0.max())
+    cap = worst_free(spec, max_len)
+    case = make_case(spec)
+    k0, v0 = case.k.clone(), case.v.clone()
+    st = RKVStep(config_of(spec, shared), spec.num_seqs, max_len, free_capacity=cap)
+    d_lens = torch.tensor(lens0, device="cuda")
+    st.device(case.cache, case.q, d_lens)   # eager warm-up: buffers, kernel attributes
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.device(case.cache, case.q, d_lens, torch.cuda.current_stream())
+    trig = spec.budget + spec.buffer
+    variants = [lens0.copy(),
+                np.where(lens0 >= trig, np.maximum(trig, lens0 - 7), lens0).astype(np.int32),
+                np.where(np.arange(spec.num_seqs) == 0, trig - 1, lens0).astype(np.int32)]
+    for i, lv in enumerate(variants):
+        case.k.copy_(k0)
+        case.v.copy_(v0)
+        d_lens.copy_(torch.from_numpy(lv))
+        st.keep.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        counts = st.d_free_counts[:spec.num_seqs].cpu().numpy()
+        total = int(counts.sum())
+        got = dict(rows=triggered_rows(spec, lv, st), k=case.k.clone(), v=case.v.clone(),
+                   lens=d_lens.cpu().numpy(), counts=counts,
+                   fb=None if st.free_blocks is None else st.free_blocks[:total].clone())
+        compare(got, host_run(spec, shared, lv, max_len, cap), f"{name} replay {i}")
+    log(f"{name}: graph replays with {len(variants)} length sets equal rkv_step")
