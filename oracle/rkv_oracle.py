@@ -35,7 +35,7 @@ __all__ = [
     "decode", "is_triggered", "window_logits", "importance", "cosine_gram",
     "redundancy", "mixed_score", "score_unit", "select_keep", "compact_rows",
     "free_blocks", "unit_step", "q_group", "step_contiguous", "step_unit",
-    "shared_score", "select_keep_shared", "layer_step_shared",
+    "shared_score", "select_keep_shared", "layer_step_shared", "redundancy_at",
 ]
 
 
@@ -97,6 +97,23 @@ def redundancy(k: np.ndarray) -> np.ndarray:
     c = cosine_gram(k)
     off = c.sum(axis=1) - np.diag(c)
     return off / (n - 1)
+
+
+def redundancy_at(k: np.ndarray, idx) -> np.ndarray:
+    """The redundancy of the tokens idx only, for caches too long for the
+    N x N Gram: for each j, row j of the cosine matrix (the cosines of key j
+    with every key), minus its diagonal entry, over N - 1.  The same
+    definition as redundancy(), one row at a time."""
+    n = k.shape[0]
+    assert n >= 2
+    norms = np.sqrt((k * k).sum(axis=1))
+    safe = np.where(norms > 0, norms, 1.0)
+    khat = np.where(norms[:, None] > 0, k / safe[:, None], 0.0)
+    out = []
+    for j in np.asarray(idx, dtype=np.int64):
+        row = khat @ khat[j]
+        out.append((row.sum() - row[j]) / (n - 1))
+    return np.array(out, dtype=np.float64)
 
 
 def mixed_score(imp: np.ndarray, red: np.ndarray, lam: float) -> np.ndarray:

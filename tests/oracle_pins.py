@@ -150,6 +150,17 @@ def pin_redundancy_rank_one_closed_form(o):
         _close(o.redundancy(k), expect, tol=1e-12)
 
 
+def pin_redundancy_rowwise_equals_gram(o):
+    """The one-row-at-a-time redundancy (for long caches) equals the Gram-based
+    one, zero keys and duplicates included."""
+    for seed in range(4):
+        _, k = _rand_case(500 + seed, 37, 16, 1, dup=3)
+        k[5] = 0.0
+        idx = [0, 5, 17, 36]
+        _close(o.redundancy_at(k, idx), o.redundancy(k)[idx])
+        _close(o.redundancy_at(k, range(37)), o.redundancy(k))
+
+
 def pin_redundancy_scale_invariant(o):
     """Cosine ignores each key's length: scaling keys by different positive
     factors leaves R unchanged."""

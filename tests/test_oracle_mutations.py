@@ -44,6 +44,9 @@ MUTANTS = [
      "qg = q_seq_layer[h::q_seq_layer.shape[0] // group]"),
     ("transposed Gram operand", "return khat @ khat.T", "return khat.T @ khat"),
     ("gather off by one", "return rows[np.asarray(keep)]", "return rows[np.minimum(np.asarray(keep) + 1, len(rows) - 1)]"),
+    ("row-wise redundancy keeps the diagonal", "out.append((row.sum() - row[j]) / (n - 1))",
+     "out.append(row.sum() / (n - 1))"),
+    ("row-wise redundancy unnormalised", "row = khat @ khat[j]", "row = k @ k[j]"),
     ("shared: max over heads", "return hs.sum(axis=0)", "return hs.max(axis=0)"),
     ("shared: first head only", "return hs.sum(axis=0)", "return hs[0]"),
     ("shared: mean over heads", "return hs.sum(axis=0)", "return hs.mean(axis=0)"),
