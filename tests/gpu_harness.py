@@ -157,7 +157,7 @@ def run_step(case, keep_parts=True, sentinel=True, shared=False, fused=False):
     if sentinel:   # rows of untriggered units must stay as they are
         step.scores.fill_(float("nan"))
         step.keep.fill_(-7)
-        if keep_parts:
+        if step.importance is not None:
             step.importance.fill_(float("nan"))
             step.redundancy.fill_(float("nan"))
     lens = case.lens0.astype(np.int32).copy()

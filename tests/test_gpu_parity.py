@@ -105,6 +105,18 @@ SMALL = {
                                       buffer=40, num_blocks=100, lens=(290, 700)),
     "runs-dups": syn.config(4).with_(name="runs", seed=22, num_seqs=2, num_layers=2,
                                      lens=(1152, 1152)),
+    # the largest window-row count the kernels accept: 71 query heads on one kv head, w = 2
+    "window-rows-142": syn.config(1).with_(name="gw142", seed=23, num_seqs=1, num_layers=1,
+                                           num_q_heads=71, num_kv_heads=1, window=2, budget=200,
+                                           buffer=40, lens=(400,)),
+    # paged block sizes at both ends of the supported range
+    "paged-bs1": syn.config(3).with_(name="p1", seed=24, num_seqs=2, num_layers=2, num_q_heads=8,
+                                     num_kv_heads=2, budget=60, buffer=10, block_size=1,
+                                     num_blocks=200, lens=(70, 90)),
+    "paged-bs1024-d64": syn.config(3).with_(name="p1024", seed=25, num_seqs=2, num_layers=2,
+                                            num_q_heads=4, num_kv_heads=2, head_dim=64,
+                                            budget=1500, buffer=100, block_size=1024,
+                                            num_blocks=8, lens=(1600, 2100)),
 }
 
 
