@@ -27,6 +27,20 @@ __device__ __forceinline__ void load_to_lds16(const void* g, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Value rows are read once: non-temporal loads.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  return make_uint4(__builtin_nontemporal_load(&p->x), __builtin_nontemporal_load(&p->y),
+                    __builtin_nontemporal_load(&p->z), __builtin_nontemporal_load(&p->w));
+}
+
+// Compacted rows are not read again by this step: non-temporal stores.
+__device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
+  __builtin_nontemporal_store(v.x, &p->x);
+  __builtin_nontemporal_store(v.y, &p->y);
+  __builtin_nontemporal_store(v.z, &p->z);
+  __builtin_nontemporal_store(v.w, &p->w);
+}
+
 // LDS of the fused kernel besides the value-row buffer.
 template <int D, int RT>
 struct StepLds {
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
       if (slot >= 0 && slot != key) {
         uint16_t* p = kbase + rows.at(slot) + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<uint4*>(p + 32 * ks) = kf[j].w[ks];
+        for (int ks = 0; ks < KS; ++ks) stream_store(reinterpret_cast<uint4*>(p + 32 * ks), kf[j].w[ks]);
       }
     }
   }
@@ -148,9 +162,9 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   const int last = max(mid - 1, 0);
 #define RKV_VLOAD(r)                     \
   const int s##r = start + r * RPP + rr; \
-  const uint4 b##r = *reinterpret_cast<const uint4*>(vget + rows.at(S.keep[min(s##r, last)]) * 2);
+  const uint4 b##r = stream_load(reinterpret_cast<const uint4*>(vget + rows.at(S.keep[min(s##r, last)]) * 2));
 #define RKV_VSTORE(r) \
-  if (s##r < mid) *reinterpret_cast<uint4*>(vdst + rows.at(s##r) * 2) = b##r;
+  if (s##r < mid) stream_store(reinterpret_cast<uint4*>(vdst + rows.at(s##r) * 2), b##r);
   RKV_VLOAD(0) RKV_VLOAD(1) RKV_VLOAD(2) RKV_VLOAD(3) RKV_VLOAD(4)
   RKV_VLOAD(5) RKV_VLOAD(6) RKV_VLOAD(7) RKV_VLOAD(8) RKV_VLOAD(9)
   RKV_VLOAD(10) RKV_VLOAD(11) RKV_VLOAD(12) RKV_VLOAD(13) RKV_VLOAD(14)
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
 #undef RKV_VSTORE
   for (int s = mid + rr; s < budget; s += RPP) {
     const uint4 v = *reinterpret_cast<const uint4*>(vbuf + (S.keep[s] - pb) * SS::ROWB + piece);
-    *reinterpret_cast<uint4*>(vdst + rows.at(s) * 2) = v;
+    stream_store(reinterpret_cast<uint4*>(vdst + rows.at(s) * 2), v);
   }
 
   if (PAGED && sa.free_blocks != nullptr && u.l == 0 && u.h == 0) {
