@@ -76,9 +76,9 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   for (int t0 = start; t0 < budget; t0 += TILE) {
 #define RKV_LOAD(r)                                                                  \
     const int s##r = min(t0 + r * RPP + rr, budget - 1);                             \
-    const uint4 b##r = *reinterpret_cast<const uint4*>(                              \
-        base + row_at<PAGED>(a, u, keep_s[s##r]) * esize);
-#define RKV_STORE(r) *reinterpret_cast<uint4*>(base + row_at<PAGED>(a, u, s##r) * esize) = b##r;
+    const uint4 b##r = stream_load(reinterpret_cast<const uint4*>(                   \
+        base + row_at<PAGED>(a, u, keep_s[s##r]) * esize));
+#define RKV_STORE(r) stream_store(reinterpret_cast<uint4*>(base + row_at<PAGED>(a, u, s##r) * esize), b##r);
     RKV_LOAD(0) RKV_LOAD(1) RKV_LOAD(2) RKV_LOAD(3) RKV_LOAD(4) RKV_LOAD(5) RKV_LOAD(6) RKV_LOAD(7)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -97,6 +97,20 @@ __device__ __forceinline__ int64_t out_row(const Geom& g, const Unit& u) {
   return ((int64_t)u.l * g.num_seqs + u.s) * g.hkv + u.h;
 }
 
+// 16 bytes read or written once by this step (rows being compacted):
+// non-temporal accesses, so the step's writes do not linger dirty in the
+// caches and its single-use reads do not displace other lines.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  return make_uint4(__builtin_nontemporal_load(&p->x), __builtin_nontemporal_load(&p->y),
+                    __builtin_nontemporal_load(&p->z), __builtin_nontemporal_load(&p->w));
+}
+__device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
+  __builtin_nontemporal_store(v.x, &p->x);
+  __builtin_nontemporal_store(v.y, &p->y);
+  __builtin_nontemporal_store(v.z, &p->z);
+  __builtin_nontemporal_store(v.w, &p->w);
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -27,20 +27,6 @@ __device__ __forceinline__ void load_to_lds16(const void* g, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Value rows are read once: non-temporal loads.
-__device__ __forceinline__ uint4 stream_load(const uint4* p) {
-  return make_uint4(__builtin_nontemporal_load(&p->x), __builtin_nontemporal_load(&p->y),
-                    __builtin_nontemporal_load(&p->z), __builtin_nontemporal_load(&p->w));
-}
-
-// Compacted rows are not read again by this step: non-temporal stores.
-__device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
-  __builtin_nontemporal_store(v.x, &p->x);
-  __builtin_nontemporal_store(v.y, &p->y);
-  __builtin_nontemporal_store(v.z, &p->z);
-  __builtin_nontemporal_store(v.w, &p->w);
-}
-
 // LDS of the fused kernel besides the value-row buffer.
 template <int D, int RT>
 struct StepLds {
