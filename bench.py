@@ -65,10 +65,16 @@ def fused_launch(spec, trig_lens) -> bool:
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the kernel's source code with comments and whitespace removed
+    (an edit to a comment leaves the compiled kernel, and so the counters
+    taken on it, as they were)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "kv_cache_compression_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kv_cache_compression_decode_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,9 +8,9 @@
 //   S_j = lambda I_j - (1 - lambda) R_j.
 // Phases, each over the register-resident key fragments:
 //   1. 1/|k| per key and the unit's sum of khat (DPP row sums, LDS across waves)
-//   2. per window row, the max of q.k over all keys (keys x rows MFMA)
-//   3. per window row, sum of exp2(y - max)               (same product again)
-//   4. rows x keys MFMA with the sum of khat as two extra bf16 rows: first
+//   2. per window row, the max of y = q.k scaled and the sum of exp2(y - max)
+//      in one online pass (keys x rows MFMA)
+//   3. rows x keys MFMA with the sum of khat as two extra bf16 rows: first
 //      the redundancy (tiles holding the sum rows), then the importance
 //      (window tiles) and the mixed score.
 // Window-query rows live in LDS with a padded row pitch (D + 8 elements) so
@@ -201,8 +201,8 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   }
   lds_barrier();
 
-  // 4. rows x keys (lane holds rows 4*g4 + i of key col).
-  // 4a: the tile(s) holding the sum rows give khat . sum khat, hence the
+  // 3. rows x keys (lane holds rows 4*g4 + i of key col).
+  // 3a: the tile(s) holding the sum rows give khat . sum khat, hence the
   // redundancy, which replaces 1/|k| in LDS.
   const int st0 = gw >> 4, st1 = (gw + 1) >> 4;
   const float inv_nm1 = 1.f / (float)(n - 1);
@@ -241,7 +241,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       }
     }
   }
-  // 4b: the window tiles give the importance; then the mixed score.
+  // 3b: the window tiles give the importance; then the mixed score.
   float ip[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) ip[j] = 0.f;
