@@ -49,6 +49,27 @@ struct Geom {
 // memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// LDS atomics without a return value.  Written as single instructions so
+// that the compiler, which cannot tell an atomic's target apart from the
+// LDS that global_load_lds is still filling, does not make them wait for
+// all outstanding global loads and stores.  LDS operations complete in
+// order; the next lds_barrier waits for them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_min(int* p, int v) {
+  asm volatile("ds_min_i32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_min(uint32_t* p, uint32_t v) {
+  asm volatile("ds_min_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_max(uint32_t* p, uint32_t v) {
+  asm volatile("ds_max_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+
 // Element offset of the row of token t of (layer l, sequence s, kv head h).
 __device__ __forceinline__ int64_t row_offset(const Geom& g, const int32_t* __restrict__ bt,
                                               int l, int s, int h, int t) {

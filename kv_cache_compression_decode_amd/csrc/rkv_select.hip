@@ -25,6 +25,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
     for (int h = 1; h < heads; ++h) sc += srow[(int64_t)h * a.score_stride + j];
     keys[j] = order_key(sc);
   }
+  block_select_init(sh);
   __syncthreads();
   block_select<kThreads, 0>(keys, cand, want, a.g.window, sh, [&](int i, int pos) {
     for (int h = 0; h < heads; ++h) krow[(int64_t)h * a.g.budget + i] = pos;

@@ -9,9 +9,9 @@
 // runs, and the compaction moves the same rows.
 //
 // Value rows: the last PRE rows of the unit are copied HBM -> LDS
-// (global_load_lds, no registers) as soon as the keys are on chip, so that
-// transfer overlaps the scoring and selection arithmetic; the other moved
-// value rows are read into registers after selection.  Every moved row is
+// (global_load_lds, no registers) while the scoring arithmetic runs, issued
+// in parts at its prefetch stages; the other moved value rows are read into
+// registers after selection.  Every moved row is
 // read before any is written, so the in-place move needs no ordering.
 #pragma once
 
@@ -75,13 +75,18 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   KeyFrag<true, D> kf[NBW];
   unit_score<PAGED, D, RT>(
       a, u, S.unit, kf,
-      [&] {
+      [&](int stage) {
         KeyRows<PAGED> rows;
         rows.init(a.g, a.bt, u);
         // wave w, round i: rows RPI*(w + 16 i) .. +RPI-1 of the buffer, one
-        // 16-byte piece per lane, landing at the wave's base + 16 * lane
+        // 16-byte piece per lane, landing at the wave's base + 16 * lane.
+        // The rounds are spread over the prefetch stages -- except for the
+        // paged layout, whose row addresses need block-table loads: waiting
+        // for those would also wait for the rounds already in flight.
+        constexpr int NST = PAGED ? 1 : kPrefetchStages;
+        if (stage >= NST) return;
 #pragma unroll
-        for (int i = 0; i < SS::ROUNDS; ++i) {
+        for (int i = stage * SS::ROUNDS / NST; i < (stage + 1) * SS::ROUNDS / NST; ++i) {
           const int row0 = SS::RPI * (wave + kUnitWaves * i);
           const int pos = min(pb + row0 + lane / TPR, n - 1);
           load_to_lds16(vsrc + rows.at(pos) * 2 + (lane % TPR) * 16, vbuf + row0 * SS::ROWB);
@@ -92,6 +97,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
     S.first_moved = budget;
     S.lds_from = budget;
   }
+  block_select_init(S.sel);
   lds_barrier();
 
   int32_t* krow = sa.keep + out_row(a.g, u) * budget;
@@ -113,8 +119,8 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
     if (p != i) lo = min(lo, i);
     if (p >= pb) cut = min(cut, i);
   }
-  if (lo < budget) atomicMin(&S.first_moved, lo);
-  if (cut < budget) atomicMin(&S.lds_from, cut);
+  if (lo < budget) lds_min(&S.first_moved, lo);
+  if (cut < budget) lds_min(&S.lds_from, cut);
   lds_barrier();
 
   KeyRows<PAGED> rows;
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
       if (slot >= 0 && slot != key) {
         uint16_t* p = kbase + rows.at(slot) + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) stream_store(reinterpret_cast<uint4*>(p + 32 * ks), kf[j].w[ks]);
+        for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<uint4*>(p + 32 * ks) = kf[j].w[ks];
       }
     }
   }
@@ -137,7 +143,9 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   // (passes of RPP rows, at most 20 -- the key fragments are dead by now),
   // [mid, budget) from vbuf.  The register loads are unconditional (slots
   // clamped into [start, mid)) so that no branch makes a wave wait between
-  // them; only slots below mid are stored from registers.
+  // them; only slots below mid are stored from registers.  The value rows
+  // are written with non-temporal stores (measured: faster than cached
+  // stores here, while cached loads and key stores beat non-temporal ones).
   static_assert(NMAX <= 20 * RPP, "value rows must fit 20 register passes");
   const int piece = (t % TPR) * 16;
   uint8_t* vdst = reinterpret_cast<uint8_t*>(sa.v) + piece;
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   const int last = max(mid - 1, 0);
 #define RKV_VLOAD(r)                     \
   const int s##r = start + r * RPP + rr; \
-  const uint4 b##r = stream_load(reinterpret_cast<const uint4*>(vget + rows.at(S.keep[min(s##r, last)]) * 2));
+  const uint4 b##r = *reinterpret_cast<const uint4*>(vget + rows.at(S.keep[min(s##r, last)]) * 2);
 #define RKV_VSTORE(r) \
   if (s##r < mid) stream_store(reinterpret_cast<uint4*>(vdst + rows.at(s##r) * 2), b##r);
   RKV_VLOAD(0) RKV_VLOAD(1) RKV_VLOAD(2) RKV_VLOAD(3) RKV_VLOAD(4)

@@ -9,7 +9,7 @@
 // Phases, each over the register-resident key fragments:
 //   1. 1/|k| per key and the unit's sum of khat (DPP row sums, LDS across waves)
 //   2. per window row, the max of y = q.k scaled and the sum of exp2(y - max)
-//      in one online pass (keys x rows MFMA)
+//      (keys x rows MFMA; per chunk of key blocks the max first, then the sum)
 //   3. rows x keys MFMA with the sum of khat as two extra bf16 rows: first
 //      the redundancy (tiles holding the sum rows), then the importance
 //      (window tiles) and the mixed score.
@@ -46,15 +46,21 @@ struct UnitLds {
   float rn[UnitShape<D>::NMAX];                    // 1/|k| per key, then R_j
 };
 
+// Points at which unit_score calls its prefetch hook, once each, after the
+// keys are on chip: 0 at the start of the arithmetic, 1 after the first row
+// tile of phase 2, 2 before phase 3, 3 before its importance part.  A caller
+// streaming memory that overlaps the arithmetic spreads its loads over them,
+// so that no wave waits long for room to issue a load.
+constexpr int kPrefetchStages = 4;
+
 // Loads the unit's keys into kf (blocks wave + 16 j) and scores them; calls
-// after_keys() once the keys are on chip (so that a caller can start memory
-// traffic that overlaps the arithmetic) and sink(key, S_j) once per key from
+// prefetch(stage) at the points above and sink(key, S_j) once per key from
 // the lane that holds it (after writing the score outputs).  All
 // kUnitThreads threads call it.
-template <bool PAGED, int D, int RT, typename AfterKeys, typename Sink>
+template <bool PAGED, int D, int RT, typename Prefetch, typename Sink>
 __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, UnitLds<D, RT>& L,
                                            KeyFrag<true, D> (&kf)[UnitShape<D>::NBW],
-                                           AfterKeys after_keys, Sink sink) {
+                                           Prefetch prefetch, Sink sink) {
   constexpr int KS = D / 32;
   constexpr int NBW = UnitShape<D>::NBW;
   constexpr int QP = UnitLds<D, RT>::QP;
@@ -128,58 +134,59 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     }
   }
   __syncthreads();   // window rows in LDS
-  after_keys();
+  prefetch(0);
 
-  // 2. per window row, the max of y and the sum of exp2(y - max) over all
-  // keys in one pass (keys x rows: lane holds keys 4*g4 + i of row col),
-  // rescaling the running sum whenever the running max grows
+  // 2. per window row, the max of y = q.k scaled (log2 units) and the sum of
+  // exp2(y - max) over the wave's keys (keys x rows: lane holds keys
+  // 4*g4 + i of row col).  Key blocks are taken PH2 at a time: all products
+  // of a chunk are formed before any exponential, so the chunk's row max is
+  // known first and the running sum is rescaled once per chunk.
+  constexpr int PH2 = NBW < 2 ? NBW : 2;   // more live products spill registers
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (rt >= rt1) continue;
-    bf16x8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
     float mx = -INFINITY, zz = 0.f;
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < NBW; j0 += PH2) {
+      f32x4 c[PH2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j].w[ks]), qf[ks],
-                                                    c, 0, 0, 0);
-      const int kb = (wave + kUnitWaves * j) * kBlockKeys + 4 * g4;
-      if (kb >= n) continue;   // lane-divergent; the product above is wave-wide
-      float y[4], bm = -INFINITY;
+      for (int j = 0; j < PH2; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y[i] = kb + i < n ? c[i] * a.c : -INFINITY;   // log2 units
-        bm = fmaxf(bm, y[i]);
+      for (int ks = 0; ks < KS; ++ks) {   // one 32-dim slice of the rows at a time
+        const bf16x8 qf =
+            *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
+#pragma unroll
+        for (int j = 0; j < PH2; ++j)
+          if (j0 + j < NBW)
+            c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, kf[j0 + j].w[ks]), qf, c[j], 0, 0, 0);
       }
-      const float mn = fmaxf(mx, bm);                 // finite: key kb is valid
-      float zb = 0.f;
+      float cm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) zb += fast_exp2(y[i] - mn);
-      zz = fmaf(zz, fast_exp2(mx - mn), zb);
+      for (int j = 0; j < PH2; ++j) {
+        const int kb = (wave + kUnitWaves * (j0 + j)) * kBlockKeys + 4 * g4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[j][i] = j0 + j < NBW && kb + i < n ? c[j][i] * a.c : -INFINITY;
+          cm = fmaxf(cm, c[j][i]);
+        }
+      }
+      const float mn = fmaxf(mx, xmax32(xmax16(cm)));   // same on the 4 lanes of the row
+      const float off = mn == -INFINITY ? 0.f : mn;      // no keys yet: everything adds 0
+      float zc = 0.f;
+#pragma unroll
+      for (int j = 0; j < PH2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zc += fast_exp2(c[j][i] - off);
+      zz = j0 == 0 ? zc : fmaf(zz, fast_exp2(mx - off), zc);
       mx = mn;
     }
-    // merge with the lanes holding the same row: l ^ 16, then l ^ 32
-    {
-      auto pm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      auto pz = __builtin_amdgcn_permlane16_swap(__float_as_uint(zz), __float_as_uint(zz), false, false);
-      const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
-      merge_stats_pair(m0, __uint_as_float(pz[0]), m1, __uint_as_float(pz[1]), mx, zz);
-    }
-    {
-      auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zz), __float_as_uint(zz), false, false);
-      const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
-      merge_stats_pair(m0, __uint_as_float(pz[0]), m1, __uint_as_float(pz[1]), mx, zz);
-    }
+    zz = sum_rows(zz);
     if (g4 == 0) {
       red_m[wave][rt * 16 + col] = mx;
       red_z[wave][rt * 16 + col] = zz;
     }
+    if (rt == 0) prefetch(1);
   }
   lds_barrier();
   if (t < RT * 16) {
@@ -201,6 +208,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   }
   lds_barrier();
 
+  prefetch(2);
   // 3. rows x keys (lane holds rows 4*g4 + i of key col).
   // 3a: the tile(s) holding the sum rows give khat . sum khat, hence the
   // redundancy, which replaces 1/|k| in LDS.
@@ -241,6 +249,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       }
     }
   }
+  prefetch(3);
   // 3b: the window tiles give the importance; then the mixed score.
   float ip[NBW];
 #pragma unroll
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(kUnitThreads) void score_unit_kernel(ScoreArgs a) {
   KeyFrag<true, D> kf[UnitShape<D>::NBW];
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
   if (u.n == 0) return;   // past the device table's count
-  unit_score<PAGED, D, RT>(a, u, L, kf, [] {}, [](int, float) {});
+  unit_score<PAGED, D, RT>(a, u, L, kf, [](int) {}, [](int, float) {});
 }
 
 
