@@ -77,6 +77,14 @@ __device__ __forceinline__ float sum_in_row(float v) {
   v = dpp_add<0x140>(v);   // row_mirror
   return v;
 }
+// Max over the 16 lanes of a row, likewise.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true)));
+}
+__device__ __forceinline__ float max_in_row(float v) {
+  return dpp_max<0x140>(dpp_max<0x141>(dpp_max<0x4E>(dpp_max<0xB1>(v))));
+}
 
 // 2^x and 1/sqrt(x) as single hardware instructions (v_exp_f32, v_rsq_f32).
 // Arguments of the exponentials are <= 0 (logit minus its running max), so

@@ -39,9 +39,11 @@ struct UnitLds {
   static constexpr int QITEMS = RT * 16 * (D / 8);
   static constexpr int QPER = (QITEMS + kUnitThreads - 1) / kUnitThreads;
   __attribute__((aligned(16))) uint16_t q[(RT * 16 + 1) * QP];
-  float red_m[kUnitWaves][RT * 16];
-  float red_z[kUnitWaves][RT * 16];
-  float red_s[kUnitWaves][D];
+  // per-wave partials, wave index last: the 16 lanes that merge one row (or
+  // one dim) read 16 consecutive words
+  float red_m[RT * 16][kUnitWaves];
+  float red_z[RT * 16][kUnitWaves];
+  float red_s[D][kUnitWaves];
   float row_m[RT * 16], row_iz[RT * 16];
   float rn[UnitShape<D>::NMAX];                    // 1/|k| per key, then R_j
 };
@@ -130,17 +132,24 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     for (int e = 0; e < 8; ++e) s8[e] = sum_in_row(s8[e]);
     if (col == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red_s[wave][32 * ks + 8 * g4 + e] = s8[e];
+      for (int e = 0; e < 8; ++e) red_s[32 * ks + 8 * g4 + e][wave] = s8[e];
     }
   }
   __syncthreads();   // window rows in LDS
   prefetch(0);
 
+  // the wave's key blocks that hold a key: blocks wave + 16 j, j < nbl
+  const int nbl = __builtin_amdgcn_readfirstlane((n - wave * kBlockKeys + kUnitWaves * kBlockKeys - 1) /
+                                                 (kUnitWaves * kBlockKeys));
   // 2. per window row, the max of y = q.k scaled (log2 units) and the sum of
   // exp2(y - max) over the wave's keys (keys x rows: lane holds keys
   // 4*g4 + i of row col).  Key blocks are taken PH2 at a time: all products
   // of a chunk are formed before any exponential, so the chunk's row max is
-  // known first and the running sum is rescaled once per chunk.
+  // known first and the running sum is rescaled once per chunk.  The
+  // exponent is one fma of the raw product: exp2(p * c - max).  Blocks past
+  // the unit's end are skipped (a wave-uniform test).  Keys past the end in
+  // a lane's last block were loaded as copies of the last key: they leave
+  // the max unchanged, and the sum leaves them out.
   constexpr int PH2 = NBW < 2 ? NBW : 2;   // more live products spill registers
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -148,6 +157,10 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     float mx = -INFINITY, zz = 0.f;
 #pragma unroll
     for (int j0 = 0; j0 < NBW; j0 += PH2) {
+      if (j0 >= nbl) continue;
+      bool live[PH2];
+#pragma unroll
+      for (int j = 0; j < PH2; ++j) live[j] = j0 + j < NBW && j0 + j < nbl;
       f32x4 c[PH2];
 #pragma unroll
       for (int j = 0; j < PH2; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -157,54 +170,63 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
             *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
 #pragma unroll
         for (int j = 0; j < PH2; ++j)
-          if (j0 + j < NBW)
+          if (live[j])
             c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8, kf[j0 + j].w[ks]), qf, c[j], 0, 0, 0);
       }
-      float cm = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < PH2; ++j) {
-        const int kb = (wave + kUnitWaves * (j0 + j)) * kBlockKeys + 4 * g4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c[j][i] = j0 + j < NBW && kb + i < n ? c[j][i] * a.c : -INFINITY;
-          cm = fmaxf(cm, c[j][i]);
-        }
-      }
-      const float mn = fmaxf(mx, xmax32(xmax16(cm)));   // same on the 4 lanes of the row
-      const float off = mn == -INFINITY ? 0.f : mn;      // no keys yet: everything adds 0
-      float zc = 0.f;
+      float cm = -INFINITY;   // max of the raw products (the scale a.c > 0 keeps the order)
 #pragma unroll
       for (int j = 0; j < PH2; ++j)
+        if (live[j])
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zc += fast_exp2(c[j][i] - off);
-      zz = j0 == 0 ? zc : fmaf(zz, fast_exp2(mx - off), zc);
+          for (int i = 0; i < 4; ++i) cm = fmaxf(cm, c[j][i]);
+      const float mn = fmaxf(mx, xmax32(xmax16(cm)));   // same on the 4 lanes of the row
+      const float off = mn * a.c;                        // log2 units; finite: a key is live
+      float zc = 0.f;
+#pragma unroll
+      for (int j = 0; j < PH2; ++j) {
+        if (!live[j]) continue;
+        const int nv = n - (wave + kUnitWaves * (j0 + j)) * kBlockKeys - 4 * g4;   // valid of the 4
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(fmaf(c[j][i], a.c, -off));
+          zc += i < nv ? e : 0.f;
+        }
+      }
+      zz = j0 == 0 ? zc : fmaf(zz, fast_exp2(fmaf(mx, a.c, -off)), zc);
       mx = mn;
     }
     zz = sum_rows(zz);
     if (g4 == 0) {
-      red_m[wave][rt * 16 + col] = mx;
-      red_z[wave][rt * 16 + col] = zz;
+      red_m[rt * 16 + col][wave] = mx == -INFINITY ? mx : mx * a.c;   // log2 units
+      red_z[rt * 16 + col][wave] = zz;
     }
     if (rt == 0) prefetch(1);
   }
   lds_barrier();
-  if (t < RT * 16) {
-    float mm = -INFINITY, zz = 0.f;
-    if (t < gw) {
-#pragma unroll
-      for (int w = 0; w < kUnitWaves; ++w) merge_stats(mm, zz, red_m[w][t], red_z[w][t]);
+  // the waves' partials merged by rows of 16 lanes (lane = wave): per
+  // window row the max and the rescaled sum; per dim the sum of khat, split
+  // into the two bf16 rows gw and gw + 1.  Trip counts are wave-uniform
+  // (RT * 256 and D * 16 are multiples of 64).
+  static_assert(kUnitWaves == 16, "one DPP row of lanes per merged row");
+  for (int idx = t; idx < RT * 16 * kUnitWaves; idx += kUnitThreads) {
+    const int r = idx / kUnitWaves, w = idx % kUnitWaves;
+    const float m = r < gw ? red_m[r][w] : -INFINITY;
+    const float mm = max_in_row(m);
+    const float z = sum_in_row(mm == -INFINITY ? 0.f : red_z[r][w] * fast_exp2(m - mm));
+    if (w == 0) {
+      row_m[r] = r < gw ? mm : INFINITY;   // log2 units; other rows add nothing
+      row_iz[r] = r < gw ? 1.f / (z * (float)gw) : 0.f;
     }
-    row_m[t] = t < gw ? mm : INFINITY;   // log2 units; other rows add nothing
-    row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
   }
-  if (t < D) {   // sum of khat, split into the two bf16 rows gw and gw + 1
-    float sv = 0.f;
-#pragma unroll
-    for (int w = 0; w < kUnitWaves; ++w) sv += red_s[w][t];
-    const uint32_t hi = f2bf_bits(sv);
-    q_lds[gw * QP + t] = (uint16_t)hi;
-    q_lds[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
+  for (int idx = t; idx < D * kUnitWaves; idx += kUnitThreads) {
+    const int d = idx / kUnitWaves, w = idx % kUnitWaves;
+    const float sv = sum_in_row(red_s[d][w]);
+    if (w == 0) {
+      const uint32_t hi = f2bf_bits(sv);
+      q_lds[gw * QP + d] = (uint16_t)hi;
+      q_lds[(gw + 1) * QP + d] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
+    }
   }
   lds_barrier();
 
@@ -227,6 +249,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
         qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
+        if (j >= nbl) continue;   // past the end (wave-uniform)
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -269,6 +292,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
+      if (j >= nbl) continue;   // past the end (wave-uniform)
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
