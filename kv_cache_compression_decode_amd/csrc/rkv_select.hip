@@ -27,9 +27,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   }
   block_select_init(sh);
   __syncthreads();
-  block_select<kThreads, 0>(keys, cand, want, a.g.window, sh, [&](int i, int pos) {
-    for (int h = 0; h < heads; ++h) krow[(int64_t)h * a.g.budget + i] = pos;
-  });
+  block_select<kThreads, 0>(
+      keys, cand, want, a.g.window, sh,
+      [&](int i, int pos) {
+        for (int h = 0; h < heads; ++h) krow[(int64_t)h * a.g.budget + i] = pos;
+      },
+      [](int) {});
 }
 
 hipError_t prepare_select() {

@@ -149,13 +149,15 @@ __device__ __forceinline__ void hist_add(int* hist, int dg, bool on) {
 
 // keys[0, cand) hold order keys of the candidates (written before a
 // barrier that also follows block_select_init); calls out(i, position) for
-// every kept slot i in [0, budget), where budget = want + window.  All
-// THREADS threads call it.  MAXPER > 0: every thread holds at most MAXPER
-// candidates (cand <= THREADS * MAXPER), kept in registers; MAXPER = 0: any
-// cand, read from LDS on every pass.
-template <int THREADS, int MAXPER, typename OutFn>
+// every kept slot i in [0, budget), where budget = want + window, and
+// drop(position) for every candidate not kept.  All THREADS threads call it.
+// MAXPER > 0: every thread holds at most MAXPER candidates (cand <= THREADS *
+// MAXPER), kept in registers, and keys[] is not read after the first barrier
+// (the caller may reuse it from the callbacks on); MAXPER = 0: any cand, read
+// from LDS on every pass.
+template <int THREADS, int MAXPER, typename OutFn, typename DropFn>
 __device__ __forceinline__ void block_select(const uint32_t* keys, int cand, int want, int window,
-                                             SelectShared<THREADS>& sh, OutFn out) {
+                                             SelectShared<THREADS>& sh, OutFn out, DropFn drop) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   // each thread owns the contiguous positions [lo, hi); an odd run length
   // keeps the lanes of a wave on different LDS banks
@@ -249,7 +251,10 @@ __device__ __forceinline__ void block_select(const uint32_t* keys, int cand, int
         const uint32_t kk = kr[i] & mask;
         bool kp = kk > prefix;
         if (kk == prefix) kp = eqi++ < r;
-        if (kp) out(o++, lo + i);
+        if (kp)
+          out(o++, lo + i);
+        else
+          drop(lo + i);
       }
     }
   } else {
@@ -257,7 +262,10 @@ __device__ __forceinline__ void block_select(const uint32_t* keys, int cand, int
       const uint32_t kk = keys[j] & mask;
       bool kp = kk > prefix;
       if (kk == prefix) kp = eqi++ < r;
-      if (kp) out(o++, j);
+      if (kp)
+        out(o++, j);
+      else
+        drop(j);
     }
   }
   for (int i = tid; i < window; i += THREADS) out(want + i, cand + i);

@@ -100,27 +100,30 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
   block_select_init(S.sel);
   lds_barrier();
 
+  // The selection hands every token its destination slot (-1: evicted) in
+  // dest, which takes over the order keys' LDS (they live in registers after
+  // the selection's first barrier), and the keep list; meanwhile each thread
+  // notes the first slot that moves and the first slot whose row is in vbuf
+  // (keep is ascending).
   int32_t* krow = sa.keep + out_row(a.g, u) * budget;
+  int* dest = reinterpret_cast<int*>(S.keys);
+  int lo = budget, cut = budget;
   block_select<kUnitThreads, (NMAX + kUnitThreads - 1) / kUnitThreads>(
-      S.keys, n - window, budget - window, window, S.sel, [&](int i, int pos) {
+      S.keys, n - window, budget - window, window, S.sel,
+      [&](int i, int pos) {
         S.keep[i] = pos;
         krow[i] = pos;
-      });
-  lds_barrier();
-  // destination slot of every token (-1: evicted); first slot that moves;
-  // first slot whose row is in vbuf (keep is ascending)
-  int* dest = reinterpret_cast<int*>(S.keys);
-  for (int j = t; j < n; j += kUnitThreads) dest[j] = -1;
-  lds_barrier();
-  int lo = budget, cut = budget;
-  for (int i = t; i < budget; i += kUnitThreads) {
-    const int p = S.keep[i];
-    dest[p] = i;
-    if (p != i) lo = min(lo, i);
-    if (p >= pb) cut = min(cut, i);
+        dest[pos] = i;
+        if (pos != i) lo = min(lo, i);
+        if (pos >= pb) cut = min(cut, i);
+      },
+      [&](int pos) { dest[pos] = -1; });
+  lo = (int)wave_minmax<false>((uint32_t)lo);   // slots are non-negative
+  cut = (int)wave_minmax<false>((uint32_t)cut);
+  if (lane == 0) {
+    if (lo < budget) lds_min(&S.first_moved, lo);
+    if (cut < budget) lds_min(&S.lds_from, cut);
   }
-  if (lo < budget) lds_min(&S.first_moved, lo);
-  if (cut < budget) lds_min(&S.lds_from, cut);
   lds_barrier();
 
   KeyRows<PAGED> rows;
