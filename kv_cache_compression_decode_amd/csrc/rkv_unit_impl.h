@@ -49,10 +49,10 @@ struct UnitLds {
 };
 
 // Points at which unit_score calls its prefetch hook, once each, after the
-// keys are on chip: 0 at the start of the arithmetic, 1 after the first row
-// tile of phase 2, 2 before phase 3, 3 before its importance part.  A caller
-// streaming memory that overlaps the arithmetic spreads its loads over them,
-// so that no wave waits long for room to issue a load.
+// keys are on chip: 0 after phase 2, 1 before phase 3, 2 before its
+// importance part, 3 after it.  A caller streaming memory that overlaps the
+// arithmetic spreads its loads over them, so that no wave waits long for
+// room to issue a load.
 constexpr int kPrefetchStages = 4;
 
 // Loads the unit's keys into kf (blocks wave + 16 j) and scores them; calls
@@ -93,11 +93,18 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   }
   __builtin_amdgcn_sched_barrier(0);   // window-row loads issue before the key loads
   // keys of blocks wave + 16 j into registers; a lane past the end loads the
-  // unit's last key, which every later use masks out
+  // unit's last key, which every later use masks out.  The first KE blocks
+  // are requested before the barrier that publishes the window rows, the
+  // rest after it, so that barrier is not held up by waves still waiting for
+  // room to issue loads, and each wave starts phases 1-2 as soon as its own
+  // keys arrive.  (Paged rows need block-table loads for their addresses;
+  // waiting for those after the barrier would also wait for the keys already
+  // requested, so the paged layout requests every block first.)
+  constexpr int KE = PAGED ? NBW : (NBW < 2 ? NBW : 2);
   KeyRows<PAGED> rows;
   rows.init(a.g, a.bt, u);
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) {
+  for (int j = 0; j < KE; ++j) {
     const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
     kf[j].load(a.k, rows.at(min(key, n - 1)), g4, true);
   }
@@ -108,6 +115,12 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     const int r = min(i / (D / 8), RT * 16), c8 = i % (D / 8);
     const uint4 v = r < gw ? qv[p] : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(q_lds + r * QP + 8 * c8) = v;
+  }
+  lds_barrier();   // window rows in LDS
+#pragma unroll
+  for (int j = KE; j < NBW; ++j) {
+    const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
+    kf[j].load(a.k, rows.at(min(key, n - 1)), g4, true);
   }
 
   // 1. 1/|k| and the sum of khat
@@ -135,8 +148,6 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       for (int e = 0; e < 8; ++e) red_s[32 * ks + 8 * g4 + e][wave] = s8[e];
     }
   }
-  __syncthreads();   // window rows in LDS
-  prefetch(0);
 
   // the wave's key blocks that hold a key: blocks wave + 16 j, j < nbl
   const int nbl = __builtin_amdgcn_readfirstlane((n - wave * kBlockKeys + kUnitWaves * kBlockKeys - 1) /
@@ -201,9 +212,9 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       red_m[rt * 16 + col][wave] = mx == -INFINITY ? mx : mx * a.c;   // log2 units
       red_z[rt * 16 + col][wave] = zz;
     }
-    if (rt == 0) prefetch(1);
   }
-  lds_barrier();
+  lds_barrier();   // every wave's partials in LDS
+  prefetch(0);
   // the waves' partials merged by rows of 16 lanes (lane = wave): per
   // window row the max and the rescaled sum; per dim the sum of khat, split
   // into the two bf16 rows gw and gw + 1.  Trip counts are wave-uniform
@@ -230,7 +241,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   }
   lds_barrier();
 
-  prefetch(2);
+  prefetch(1);
   // 3. rows x keys (lane holds rows 4*g4 + i of key col).
   // 3a: the tile(s) holding the sum rows give khat . sum khat, hence the
   // redundancy, which replaces 1/|k| in LDS.
@@ -272,7 +283,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       }
     }
   }
-  prefetch(3);
+  prefetch(2);
   // 3b: the window tiles give the importance; then the mixed score.
   float ip[NBW];
 #pragma unroll
@@ -302,6 +313,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
       for (int i = 0; i < 4; ++i) ip[j] = fmaf(fast_exp2(fmaf(c[i], a.c, -mr[i])), iz[i], ip[j]);
     }
   }
+  prefetch(3);
   const int64_t orow = out_row(a.g, u) * a.score_stride;
   float* const s_row = a.scores + orow;
   float* const i_row = a.imp != nullptr ? a.imp + orow : nullptr;
