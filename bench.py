@@ -114,8 +114,19 @@ def cpu_baseline(spec, case, seconds: float):
     dt = time.perf_counter() - t0
     steps_per_s = done / dt / len(units)
     return {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{done} of the step's {len(units)} units (float64 numpy, explicit N x N "
                       f"Gram), {dt:.1f} s; value = units/s / units per step"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
