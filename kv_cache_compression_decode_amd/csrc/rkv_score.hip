@@ -1,5 +1,6 @@
 // Host launcher of the scoring pass: the single-pass kernel of
-// rkv_unit_impl.h for bf16 units that fit on chip, else the two kernels of
+// rkv_unit_impl.h for bf16 units that fit on chip, the key-span kernel of
+// rkv_long_impl.h for longer bf16 units, else the two kernels of
 // rkv_score_impl.h (one translation unit per cache dtype, head_dim, layout).
 #include "rkv_step_impl.h"
 
@@ -13,6 +14,10 @@ hipError_t dispatch_step_bf16_d64_contig(const StepArgs&, int, int, hipStream_t)
 hipError_t dispatch_step_bf16_d64_paged(const StepArgs&, int, int, hipStream_t);
 hipError_t dispatch_step_bf16_d128_contig(const StepArgs&, int, int, hipStream_t);
 hipError_t dispatch_step_bf16_d128_paged(const StepArgs&, int, int, hipStream_t);
+hipError_t dispatch_long_bf16_d64_contig(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_long_bf16_d64_paged(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_long_bf16_d128_contig(const ScoreArgs&, int, int, hipStream_t);
+hipError_t dispatch_long_bf16_d128_paged(const ScoreArgs&, int, int, hipStream_t);
 
 bool score_single_pass(const ScoreArgs& a, bool bf16, int max_len) {
   const int rt2 = (a.gw + 2 + 15) / 16;
@@ -32,6 +37,16 @@ hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st) {
                        : dispatch_unit_bf16_d64_contig(a, units, rt2, st);
     return a.g.paged ? dispatch_unit_bf16_d128_paged(a, units, rt2, st)
                      : dispatch_unit_bf16_d128_contig(a, units, rt2, st);
+  }
+  if (bf16 && rt2 <= kUnitMaxRowTiles) {
+    // longer bf16 units: key spans of at most NMAX keys on C workgroups each
+    const int nmax = a.g.d == 64 ? UnitShape<64>::NMAX : UnitShape<128>::NMAX;
+    const int chunks = (a.max_len + nmax - 1) / nmax;
+    if (a.g.d == 64)
+      return a.g.paged ? dispatch_long_bf16_d64_paged(a, chunks, rt2, st)
+                       : dispatch_long_bf16_d64_contig(a, chunks, rt2, st);
+    return a.g.paged ? dispatch_long_bf16_d128_paged(a, chunks, rt2, st)
+                     : dispatch_long_bf16_d128_contig(a, chunks, rt2, st);
   }
 #define RKV_PICK(DT, D)                                                              \
   return a.g.paged ? dispatch_score_##DT##_d##D##_paged(a, grid, rt1, rt2, st)       \

@@ -1,4 +1,5 @@
 // Scoring kernels instantiated for bf16 caches, head_dim 128, paged layout.
+#include "rkv_long_impl.h"
 #include "rkv_step_impl.h"
 
 namespace rkv {
@@ -11,5 +12,8 @@ hipError_t dispatch_unit_bf16_d128_paged(const ScoreArgs& a, int units, int rt2,
 }
 hipError_t dispatch_step_bf16_d128_paged(const StepArgs& a, int units, int rt2, hipStream_t st) {
   return dispatch_step<true, 128>(a, units, rt2, st);
+}
+hipError_t dispatch_long_bf16_d128_paged(const ScoreArgs& a, int chunks, int rt2, hipStream_t st) {
+  return dispatch_long<true, 128>(a, chunks, rt2, st);
 }
 }  // namespace rkv

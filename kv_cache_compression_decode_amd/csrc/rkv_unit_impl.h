@@ -55,14 +55,21 @@ struct UnitLds {
 // room to issue a load.
 constexpr int kPrefetchStages = 4;
 
-// Loads the unit's keys into kf (blocks wave + 16 j) and scores them; calls
-// prefetch(stage) at the points above and sink(key, S_j) once per key from
-// the lane that holds it (after writing the score outputs).  All
-// kUnitThreads threads call it.
-template <bool PAGED, int D, int RT, typename Prefetch, typename Sink>
-__device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, UnitLds<D, RT>& L,
-                                           KeyFrag<true, D> (&kf)[UnitShape<D>::NBW],
-                                           Prefetch prefetch, Sink sink) {
+// Loads keys [k0, k0 + nl) of the unit into kf (blocks wave + 16 j of the
+// span) and scores them; calls prefetch(stage) at the points above and
+// sink(key, S_j) once per key of the span (index within the span) from the
+// lane that holds it (after writing the score outputs).  All kUnitThreads
+// threads call it.  SPAN = false: the span is the whole unit.  SPAN = true:
+// the unit is split over several workgroups; after the span's own row
+// statistics and direction sum are in LDS (row_m, row_iz = the span's raw
+// sum, red_s[d][0]), exchange() must replace them by the unit's: row_m,
+// row_iz as below and the two direction-sum rows of q.
+template <bool PAGED, int D, int RT, bool SPAN, typename Prefetch, typename Sink,
+          typename Exchange>
+__device__ __forceinline__ void unit_score_span(const ScoreArgs& a, const Unit& u, int k0, int nl,
+                                                UnitLds<D, RT>& L,
+                                                KeyFrag<true, D> (&kf)[UnitShape<D>::NBW],
+                                                Prefetch prefetch, Sink sink, Exchange exchange) {
   constexpr int KS = D / 32;
   constexpr int NBW = UnitShape<D>::NBW;
   constexpr int QP = UnitLds<D, RT>::QP;
@@ -77,7 +84,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int col = lane & 15, g4 = lane >> 4;
   const int t = threadIdx.x;
-  const int n = u.n;
+  const int n = nl;           // keys of the span
   const int gw = a.gw, rt1 = (gw + 15) >> 4;
   // Loads are unconditional (addresses clamped into the unit) so that no
   // branch makes a wave wait on one load before issuing the next.  The
@@ -106,7 +113,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
-    kf[j].load(a.k, rows.at(min(key, n - 1)), g4, true);
+    kf[j].load(a.k, rows.at(k0 + min(key, n - 1)), g4, true);
   }
   // window rows into LDS; rows >= gw are zero until the sum rows are written
 #pragma unroll
@@ -120,7 +127,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
 #pragma unroll
   for (int j = KE; j < NBW; ++j) {
     const int key = (wave + kUnitWaves * j) * kBlockKeys + col;
-    kf[j].load(a.k, rows.at(min(key, n - 1)), g4, true);
+    kf[j].load(a.k, rows.at(k0 + min(key, n - 1)), g4, true);
   }
 
   // 1. 1/|k| and the sum of khat
@@ -226,19 +233,29 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     const float mm = max_in_row(m);
     const float z = sum_in_row(mm == -INFINITY ? 0.f : red_z[r][w] * fast_exp2(m - mm));
     if (w == 0) {
-      row_m[r] = r < gw ? mm : INFINITY;   // log2 units; other rows add nothing
-      row_iz[r] = r < gw ? 1.f / (z * (float)gw) : 0.f;
+      if (SPAN) {
+        row_m[r] = mm;
+        row_iz[r] = z;
+      } else {
+        row_m[r] = r < gw ? mm : INFINITY;   // log2 units; other rows add nothing
+        row_iz[r] = r < gw ? 1.f / (z * (float)gw) : 0.f;
+      }
     }
   }
   for (int idx = t; idx < D * kUnitWaves; idx += kUnitThreads) {
     const int d = idx / kUnitWaves, w = idx % kUnitWaves;
-    const float sv = sum_in_row(red_s[d][w]);
+    const float sv = sum_in_row(red_s[d][w]);   // the row group read all 16 before this write
     if (w == 0) {
-      const uint32_t hi = f2bf_bits(sv);
-      q_lds[gw * QP + d] = (uint16_t)hi;
-      q_lds[(gw + 1) * QP + d] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
+      if (SPAN) {
+        red_s[d][0] = sv;
+      } else {
+        const uint32_t hi = f2bf_bits(sv);
+        q_lds[gw * QP + d] = (uint16_t)hi;
+        q_lds[(gw + 1) * QP + d] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
+      }
     }
   }
+  if (SPAN) exchange();
   lds_barrier();
 
   prefetch(1);
@@ -246,7 +263,7 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
   // 3a: the tile(s) holding the sum rows give khat . sum khat, hence the
   // redundancy, which replaces 1/|k| in LDS.
   const int st0 = gw >> 4, st1 = (gw + 1) >> 4;
-  const float inv_nm1 = 1.f / (float)(n - 1);
+  const float inv_nm1 = 1.f / (float)(u.n - 1);   // the whole unit's N
   {
     float sd[NBW];
 #pragma unroll
@@ -325,12 +342,19 @@ __device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, Un
     if (g4 == 0 && key < n) {
       const float red = rn_lds[key];
       const float sc = a.lambda * ipj - (1.f - a.lambda) * red;
-      s_row[key] = sc;
-      if (i_row) i_row[key] = ipj;
-      if (r_row) r_row[key] = red;
+      s_row[k0 + key] = sc;
+      if (i_row) i_row[k0 + key] = ipj;
+      if (r_row) r_row[k0 + key] = red;
       sink(key, sc);
     }
   }
+}
+
+template <bool PAGED, int D, int RT, typename Prefetch, typename Sink>
+__device__ __forceinline__ void unit_score(const ScoreArgs& a, const Unit& u, UnitLds<D, RT>& L,
+                                           KeyFrag<true, D> (&kf)[UnitShape<D>::NBW],
+                                           Prefetch prefetch, Sink sink) {
+  unit_score_span<PAGED, D, RT, false>(a, u, 0, u.n, L, kf, prefetch, sink, [] {});
 }
 
 template <bool PAGED, int D, int RT>
