@@ -10,13 +10,15 @@
 // the C records in span order (so the C workgroups compute identical unit
 // statistics) and finishes its own keys' importance, redundancy and score.
 //
-// The grid is persistent: as many workgroups as fit on the device at once,
-// unit u of round r taken by workgroups C*(u - r*P) .. +C-1 (P units per
-// round), so the C workgroups a span waits for run in the same round of an
-// all-resident grid.  The wait is a bounded spin on a per-unit counter
-// (zeroed by a small kernel first); the bound only keeps a misconfigured
-// launch from hanging, it is never reached when the grid is resident.
+// Units are launched P at a time (P * C workgroups: as many as are resident
+// on the device at once), unit unit0 + i taken by workgroups C*i .. C*i+C-1,
+// so the C workgroups a span waits for are all running.  The wait is a
+// bounded spin on a per-unit counter (zeroed by a small kernel first); the
+// bound only keeps a misconfigured launch from hanging, it is never reached
+// when the launch is resident.
 #pragma once
+
+#include <algorithm>
 
 #include "rkv_unit_impl.h"
 
@@ -25,6 +27,7 @@ namespace rkv {
 struct LongArgs {
   int32_t chunks;       // C: workgroups (key spans) per unit
   int32_t wait_ticks;   // bound on the wait for the other spans (s_memrealtime, 100 MHz)
+  int32_t unit0;        // first unit of this launch: workgroup w takes span w % C of unit0 + w / C
 };
 
 // Counter of unit ui: the first word of record slot C of the unit (the
@@ -38,66 +41,85 @@ static __global__ void long_zero_kernel(ScoreArgs a, int C, int units) {
   if (ui < units) *long_counter(a, ui, C) = 0u;
 }
 
+// Every thread's earlier global stores are published, then this workgroup
+// adds one to the unit's counter and waits until it reaches target (or the
+// time bound passes).  All threads call it.
+__device__ __forceinline__ void span_signal_wait(uint32_t* cnt, uint32_t target, int wait_ticks) {
+  __syncthreads();   // every store of the workgroup performed
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+           __builtin_amdgcn_s_memrealtime() - t_start < (uint64_t)wait_ticks)
+      __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// The span's record (row max, raw sum, direction sum) into slot c of the
+// unit's records; identity values for a span without keys.
+template <int D, int RT>
+__device__ __forceinline__ void publish_span_stats(UnitLds<D, RT>& L, float* recs, int rec, int c,
+                                                   int gw, bool empty) {
+  __syncthreads();   // the span's statistics are in LDS
+  const int t = threadIdx.x;
+  float* mine = recs + (size_t)c * rec;
+  if (t < gw) {
+    mine[t] = empty ? -INFINITY : L.row_m[t];
+    mine[gw + t] = empty ? 0.f : L.row_iz[t];
+  }
+  if (t < D) mine[2 * gw + t] = empty ? 0.f : L.red_s[t][0];
+}
+
+// The unit's row statistics and direction-sum rows from the C records,
+// merged in span order (every span computes the same values).
+template <int D, int RT>
+__device__ __forceinline__ void merge_span_stats(UnitLds<D, RT>& L, const float* recs, int rec, int C,
+                                                 int gw) {
+  constexpr int QP = UnitLds<D, RT>::QP;
+  const int t = threadIdx.x;
+  if (t < RT * 16) {
+    float mm = -INFINITY, zz = 0.f;
+    if (t < gw)
+      for (int cc = 0; cc < C; ++cc)
+        merge_stats(mm, zz, recs[(size_t)cc * rec + t], recs[(size_t)cc * rec + gw + t]);
+    L.row_m[t] = t < gw ? mm : INFINITY;   // log2 units; other rows add nothing
+    L.row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
+  }
+  if (t < D) {   // the unit's sum of khat, split into the two bf16 rows gw and gw + 1
+    float sv = 0.f;
+    for (int cc = 0; cc < C; ++cc) sv += recs[(size_t)cc * rec + 2 * gw + t];
+    const uint32_t hi = f2bf_bits(sv);
+    L.q[gw * QP + t] = (uint16_t)hi;
+    L.q[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
+  }
+}
+
 template <bool PAGED, int D, int RT>
 __global__ __launch_bounds__(kUnitThreads) void score_long_kernel(ScoreArgs a, LongArgs la) {
   __shared__ UnitLds<D, RT> L;
   KeyFrag<true, D> kf[UnitShape<D>::NBW];
-  constexpr int QP = UnitLds<D, RT>::QP;
   const int C = la.chunks;
-  const int per_round = gridDim.x / C;
-  const int w = blockIdx.x;
-  if (w >= per_round * C) return;   // no unit for this workgroup in any round
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
-  const int c = w % C, t = threadIdx.x, gw = a.gw;
-
-  for (int u0 = 0; u0 < units; u0 += per_round) {
-    const int ui = u0 + w / C;
-    if (ui >= units) break;
+  const int c = blockIdx.x % C, t = threadIdx.x, gw = a.gw;
+  {
+    const int ui = la.unit0 + blockIdx.x / C;
+    if (ui >= units) return;
     const Unit u = decode_unit(a.g, a.tt, ui);
-    if (u.n == 0) continue;   // past the device table's count: all C workgroups skip it
+    if (u.n == 0) return;   // past the device table's count: all C workgroups skip it
     const int k0 = (int)((int64_t)c * u.n / C), k1 = (int)((int64_t)(c + 1) * u.n / C);
     float* recs = a.part + (size_t)ui * a.max_chunks * a.rec;
     uint32_t* cnt = long_counter(a, ui, C);
 
     // publish this span's record, wait for the unit's other spans, merge
     auto exchange = [&](bool empty) {
-      __syncthreads();   // the span's statistics are in LDS
-      float* mine = recs + (size_t)c * a.rec;
-      if (t < gw) {
-        mine[t] = empty ? -INFINITY : L.row_m[t];
-        mine[gw + t] = empty ? 0.f : L.row_iz[t];
-      }
-      if (t < D) mine[2 * gw + t] = empty ? 0.f : L.red_s[t][0];
-      __syncthreads();   // every record store performed
-      if (t == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)C &&
-               __builtin_amdgcn_s_memrealtime() - t_start < (uint64_t)la.wait_ticks)
-          __builtin_amdgcn_s_sleep(2);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      }
-      __syncthreads();
-      if (empty) return;
-      if (t < RT * 16) {
-        float mm = -INFINITY, zz = 0.f;
-        if (t < gw)
-          for (int cc = 0; cc < C; ++cc)
-            merge_stats(mm, zz, recs[(size_t)cc * a.rec + t], recs[(size_t)cc * a.rec + gw + t]);
-        L.row_m[t] = t < gw ? mm : INFINITY;   // log2 units; other rows add nothing
-        L.row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
-      }
-      if (t < D) {   // the unit's sum of khat, split into the two bf16 rows gw and gw + 1
-        float sv = 0.f;
-        for (int cc = 0; cc < C; ++cc) sv += recs[(size_t)cc * a.rec + 2 * gw + t];
-        const uint32_t hi = f2bf_bits(sv);
-        L.q[gw * QP + t] = (uint16_t)hi;
-        L.q[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
-      }
+      publish_span_stats(L, recs, a.rec, c, gw, empty);
+      span_signal_wait(cnt, (uint32_t)C, la.wait_ticks);
+      if (!empty) merge_span_stats(L, recs, a.rec, C, gw);
     };
 
-    __syncthreads();   // the previous round's LDS reads are done
     if (k1 > k0)
       unit_score_span<PAGED, D, RT, true>(a, u, k0, k1 - k0, L, kf, [](int) {}, [](int, float) {},
                                           [&] { exchange(false); });
@@ -125,14 +147,18 @@ hipError_t launch_long_t(const ScoreArgs& a, int chunks, hipStream_t st) {
     if (cus <= 0 || occ <= 0) return hipErrorInvalidConfiguration;
     grid_of[dev] = cus * occ;
   }
-  const int grid = grid_of[dev];
-  if (grid < chunks) return hipErrorInvalidConfiguration;
+  const int per = grid_of[dev] / chunks;   // units whose spans are all resident at once
+  if (per < 1) return hipErrorInvalidConfiguration;
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
   hipLaunchKernelGGL(long_zero_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a, chunks, units);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LongArgs la{chunks, 2000000};   // 20 ms: far beyond any wait of a resident grid
-  hipLaunchKernelGGL((score_long_kernel<PAGED, D, RT>), dim3(grid), dim3(kUnitThreads), 0, st, a, la);
-  return hipGetLastError();
+  for (int u0 = 0; u0 < units; u0 += per) {
+    LongArgs la{chunks, 2000000, u0};   // 20 ms: far beyond any wait of a resident launch
+    const int grid = std::min(per, units - u0) * chunks;
+    hipLaunchKernelGGL((score_long_kernel<PAGED, D, RT>), dim3(grid), dim3(kUnitThreads), 0, st, a, la);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool PAGED, int D>

@@ -19,6 +19,13 @@ hipError_t dispatch_long_bf16_d64_paged(const ScoreArgs&, int, int, hipStream_t)
 hipError_t dispatch_long_bf16_d128_contig(const ScoreArgs&, int, int, hipStream_t);
 hipError_t dispatch_long_bf16_d128_paged(const ScoreArgs&, int, int, hipStream_t);
 
+namespace {
+int long_chunks(const ScoreArgs& a) {
+  const int nmax = a.g.d == 64 ? UnitShape<64>::NMAX : UnitShape<128>::NMAX;
+  return (a.max_len + nmax - 1) / nmax;
+}
+}  // namespace
+
 bool score_single_pass(const ScoreArgs& a, bool bf16, int max_len) {
   const int rt2 = (a.gw + 2 + 15) / 16;
   const int nmax = a.g.d == 64 ? UnitShape<64>::NMAX : UnitShape<128>::NMAX;
@@ -40,8 +47,7 @@ hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st) {
   }
   if (bf16 && rt2 <= kUnitMaxRowTiles) {
     // longer bf16 units: key spans of at most NMAX keys on C workgroups each
-    const int nmax = a.g.d == 64 ? UnitShape<64>::NMAX : UnitShape<128>::NMAX;
-    const int chunks = (a.max_len + nmax - 1) / nmax;
+    const int chunks = long_chunks(a);
     if (a.g.d == 64)
       return a.g.paged ? dispatch_long_bf16_d64_paged(a, chunks, rt2, st)
                        : dispatch_long_bf16_d64_contig(a, chunks, rt2, st);
