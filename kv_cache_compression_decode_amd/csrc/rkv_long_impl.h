@@ -12,10 +12,12 @@
 //
 // Units are launched P at a time (P * C workgroups: as many as are resident
 // on the device at once), unit unit0 + i taken by workgroups C*i .. C*i+C-1,
-// so the C workgroups a span waits for are all running.  The wait is a
-// bounded spin on a per-unit counter (zeroed by a small kernel first); the
-// bound only keeps a misconfigured launch from hanging, it is never reached
-// when the launch is resident.
+// so the C workgroups a span waits for are all running (work of other
+// streams can only delay some of them, never block them).  The wait is a
+// spin on a per-unit counter (zeroed by a small kernel first), bounded at
+// one second so that no launch can hang the device; a launch that reached
+// the bound would finish with wrong scores -- it is never reached when the
+// launch's workgroups are dispatched.
 #pragma once
 
 #include <algorithm>
@@ -153,7 +155,7 @@ hipError_t launch_long_t(const ScoreArgs& a, int chunks, hipStream_t st) {
   hipLaunchKernelGGL(long_zero_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a, chunks, units);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int u0 = 0; u0 < units; u0 += per) {
-    LongArgs la{chunks, 2000000, u0};   // 20 ms: far beyond any wait of a resident launch
+    LongArgs la{chunks, 100000000, u0};   // 1 s: far beyond any wait of a resident launch
     const int grid = std::min(per, units - u0) * chunks;
     hipLaunchKernelGGL((score_long_kernel<PAGED, D, RT>), dim3(grid), dim3(kUnitThreads), 0, st, a, la);
     if ((e = hipGetLastError()) != hipSuccess) return e;
