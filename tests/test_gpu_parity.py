@@ -117,6 +117,15 @@ SMALL = {
                                             num_q_heads=4, num_kv_heads=2, head_dim=64,
                                             budget=1500, buffer=100, block_size=1024,
                                             num_blocks=8, lens=(1600, 2100)),
+    # units longer than one workgroup holds are scored as key spans on several
+    # workgroups: 11 spans for the 12801-token sequence, so the 10-token one
+    # in the same launch has spans without any key
+    "spans-empty": syn.config(1).with_(name="spe", seed=26, num_seqs=2, num_layers=1,
+                                       num_q_heads=4, num_kv_heads=1, budget=9, buffer=1,
+                                       lens=(10, 12801)),
+    "spans-d64": syn.config(1).with_(name="spd", seed=27, num_seqs=1, num_layers=2, num_q_heads=4,
+                                     num_kv_heads=2, head_dim=64, budget=2000, buffer=100,
+                                     lens=(3100,)),
 }
 
 
