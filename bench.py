@@ -34,7 +34,9 @@ KERNEL_SOURCES = {
     "compact": ["rkv_compact.hip", "rkv_device.h"],
     "score": ["rkv_score_impl.h", "rkv_device.h"],
     "select": ["rkv_select.hip", "rkv_device.h"],
+    "gram": ["rkv_gram.hip", "rkv_score_impl.h", "rkv_device.h"],
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
 
 
 def parse():
@@ -50,6 +52,8 @@ def parse():
                    help="time rkv_score + rkv_select + rkv_compact instead of rkv_step")
     p.add_argument("--shared", action="store_true",
                    help="head-shared selection (one keep set per sequence and layer; three kernels)")
+    p.add_argument("--gram", action="store_true",
+                   help="time rkv_redundancy_gram (the explicit cosine Gram on the matrix cores) instead")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed region, one 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -148,6 +152,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case = PagedCase(spec) if spec.layout == "paged" else ContigCase(spec)
+    if args.gram:
+        return gram_bench(args, spec, case)
     cfg = config_of(spec, shared=args.shared)
     if args.steps is None:
         copy_bytes = case.k.numel() * case.k.element_size() * 2
@@ -290,6 +296,77 @@ def main():
                           "HIP events around the timed region / steps (one kernel per step)"),
         "moved_rows": moved_rows,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def gram_bench(args, spec, case):
+    """rkv_redundancy_gram over the workload's triggered units: every unit's
+    N x N cosine matrix on the matrix cores, reduced to its row means.  It
+    reads the cache only, so all launches use the same cache; one event pair
+    around the back-to-back launches gives the launch duration.  Algorithmic
+    work: 2 N^2 d flops per unit (every product of the unit's N x N x d Gram)."""
+    import numpy as np
+    import torch
+
+    from gpu_harness import config_of
+    from kv_cache_compression_decode_amd import binding as B
+
+    if spec.dtype != "bf16":
+        raise SystemExit(f"{spec.name}: the Gram path takes bf16 caches")
+    steps = 100 if args.steps is None else args.steps
+    cfg = config_of(spec)
+    lens0 = case.lens0.astype(np.int32)
+    maxn = int(lens0.max())
+    trig = lens0 >= spec.budget + spec.buffer
+    units = int(trig.sum()) * spec.num_layers * spec.num_kv_heads
+    red = torch.empty((spec.num_layers * spec.num_seqs * spec.num_kv_heads, maxn),
+                      dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        B.rkv_redundancy_gram(cfg, case.cache, spec.num_seqs, lens0, red, maxn, stream)
+
+    for _ in range(args.warmup):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(steps):
+        run()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    flops = sum(2.0 * int(n) ** 2 * spec.head_dim for n in lens0[trig]) * spec.num_layers * spec.num_kv_heads
+    tflops = flops / (us * 1e-6) / 1e12
+    out = {
+        "metric": "Gram redundancy passes/sec (every triggered unit's N x N cosine matrix); % MFMA roofline",
+        "value": round(1e6 / us, 2),
+        "unit": "passes/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "num_seqs": spec.num_seqs, "num_layers": spec.num_layers,
+                   "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+                   "seq_lens": sorted(set(int(x) for x in lens0)), "layout": spec.layout,
+                   "triggered_units": units},
+        "entry": "rkv_redundancy_gram",
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("gram", spec.name), "kernel": "gram",
+                     "flops_per_launch": flops},
+        "kernels": {"gram": {"us": round(us, 2)}},
+        "kernel_timing": "HIP events around the timed region / steps (one kernel per launch)",
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

@@ -140,6 +140,26 @@ rkv_status rkv_score(const rkv_config *cfg, const rkv_cache *cache, const void *
                      float *importance, float *redundancy,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* The redundancy signal alone, through the explicit cosine Gram matrix: for
+ * every key j of every triggered unit, R_j = the mean of cos(k_j, k_i) over
+ * the unit's other keys i, with cos = 0 against a zero key -- the mean
+ * off-diagonal entry of row j of the unit's N x N cosine matrix (R-KV project
+ * page, "How R-KV decides what to drop"; the blog's R-KV section).  Every one
+ * of the N^2 d products is formed on the matrix cores, from the cached bf16
+ * keys themselves with float32 sums; the 1/|k| factors are applied in float32.
+ * The values equal rkv_score's redundancy output up to rounding (that call
+ * uses the equivalent rank-one form).  No workspace.
+ *   cache       bf16 keys (v is not read)
+ *   h_seq_lens  host int32 [num_seqs], current cache lengths (not modified)
+ *   redundancy  device float32, laid out as rkv_score's scores, columns
+ *               [0, len) of triggered rows written; stride >= the longest
+ *               triggered length
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED (float32 caches, head_dim,
+ * length above RKV_MAX_LEN), RKV_ERR_HIP. */
+rkv_status rkv_redundancy_gram(const rkv_config *cfg, const rkv_cache *cache, int32_t num_seqs,
+                               const int32_t *h_seq_lens, float *redundancy, int32_t stride,
+                               void *stream);
+
 /* Step 2, selection: for each triggered unit, keep[0 .. budget-window) = the
  * chosen candidates of [0, len-window) in ascending position order, and
  * keep[budget-window .. budget) = len-window .. len-1 (the window).  Candidates

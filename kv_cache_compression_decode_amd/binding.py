@@ -32,6 +32,7 @@ RKV_MAX_WINDOW_ROWS = 142
 
 # Every function declared in include/rkv.h.
 EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_workspace_size",
+           "rkv_redundancy_gram",
            "rkv_score", "rkv_select", "rkv_compact", "rkv_step",
            "rkv_step_device_workspace_size", "rkv_step_device")
 
@@ -80,6 +81,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rkv_score.argtypes = [P(rkv_config), P(rkv_cache), c_void_p, c_int32, P(c_int32),
                               c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.rkv_score.restype = c_int32
+    lib.rkv_redundancy_gram.argtypes = [P(rkv_config), P(rkv_cache), c_int32, P(c_int32),
+                                        c_void_p, c_int32, c_void_p]
+    lib.rkv_redundancy_gram.restype = c_int32
     lib.rkv_select.argtypes = [P(rkv_config), c_int32, P(c_int32), c_void_p, c_int32, c_void_p,
                                c_void_p]
     lib.rkv_select.restype = c_int32
@@ -169,6 +173,12 @@ def rkv_score(cfg, cache, q_window, num_seqs, seq_lens, scores, score_stride,
     _check(load().rkv_score(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q_window), num_seqs,
                             _i32p(lens), _ptr(scores), score_stride, _ptr(importance),
                             _ptr(redundancy), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def rkv_redundancy_gram(cfg, cache, num_seqs, seq_lens, redundancy, stride, stream=None) -> None:
+    lens = _lens(seq_lens)
+    _check(load().rkv_redundancy_gram(ctypes.byref(cfg), ctypes.byref(cache), num_seqs,
+                                      _i32p(lens), _ptr(redundancy), stride, _stream(stream)))
 
 
 def rkv_select(cfg, num_seqs, seq_lens, scores, score_stride, keep, stream=None) -> None:

@@ -303,6 +303,42 @@ rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* 
   return RKV_OK;
 }
 
+rkv_status rkv_redundancy_gram(const rkv_config* cfg, const rkv_cache* cache, int32_t num_seqs,
+                               const int32_t* h_seq_lens, float* redundancy, int32_t stride,
+                               void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  if (cfg->dtype != RKV_DTYPE_BF16)
+    return fail(RKV_ERR_UNSUPPORTED, "rkv_redundancy_gram takes bf16 caches");
+  std::vector<Trig> trig;
+  if ((st = check_cache(cfg, cache, false)) != RKV_OK) return st;
+  if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
+  if (trig.empty()) return RKV_OK;
+  if (redundancy == nullptr) return fail(RKV_ERR_INVALID_ARG, "redundancy is NULL");
+  const int32_t maxn = max_len_of(trig, 0, trig.size());
+  if (stride < maxn)
+    return fail(RKV_ERR_INVALID_ARG, "stride %d is below the longest triggered length %d", stride,
+                maxn);
+  rkv::GramArgs a{};
+  a.g = make_geom(cfg, cache, num_seqs);
+  a.k = cache->k;
+  a.bt = cache->block_table;
+  a.red = redundancy;
+  a.stride = stride;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+    const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+    fill_table(a.tt, trig, first, cnt, nullptr);
+    a.g.num_trig = cnt;
+    a.units = cnt * cfg->num_layers * cfg->num_kv_heads;
+    a.rblocks = rkv::gram_row_blocks(max_len_of(trig, first, cnt));
+    const hipError_t e = rkv::launch_gram(a, hs);
+    if (e != hipSuccess) return hip_fail(e, "gram launch");
+  }
+  return RKV_OK;
+}
+
 rkv_status rkv_select(const rkv_config* cfg, int32_t num_seqs, const int32_t* h_seq_lens,
                       const float* scores, int32_t score_stride, int32_t* keep, void* stream) {
   g_err.clear();

@@ -67,7 +67,21 @@ struct TableArgs {
   int32_t block_size;     // paged block size; 0 for the contiguous layout
 };
 
+// Redundancy through the explicit cosine Gram matrix (rkv_redundancy_gram).
+struct GramArgs {
+  Geom g;
+  TrigTable tt;
+  const void* k;          // keys (contiguous cache or paged pool), bf16
+  const int32_t* bt;      // paged block table or nullptr
+  float* red;             // [L][S][Hkv][stride]
+  int32_t stride;
+  int32_t units;          // triggered units of this launch (num_trig * L * Hkv)
+  int32_t rblocks;        // 128-row blocks per unit: gram_row_blocks(longest length)
+};
+
 hipError_t launch_table(const TableArgs& a, hipStream_t st);
+int gram_row_blocks(int max_len);
+hipError_t launch_gram(const GramArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st);
 // true if launch_step can run this launch's units (else use the three kernels)
 bool step_fusable(const ScoreArgs& a, bool bf16);

@@ -212,3 +212,22 @@ def test_step_device_argument_errors():
     expect(B.RKV_ERR_INVALID_ARG, step_dev, pc, ca=cache(num_blocks=100, block_table=FAKE,
                                                           max_blocks=71), n=2, fb=FAKE, cap=16)
     step_dev(c, n=0)   # no sequences: nothing to do, nothing enqueued
+
+
+def gram(c, ca=None, lens=(1152,), red=FAKE, stride=1152):
+    B.rkv_redundancy_gram(c, cache() if ca is None else ca, len(lens), list(lens), red, stride,
+                          None)
+
+
+def test_gram_argument_errors():
+    c = cfg()
+    expect(B.RKV_ERR_UNSUPPORTED, gram, cfg(dtype="f32"))
+    expect(B.RKV_ERR_UNSUPPORTED, gram, cfg(head_dim=96))
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, ca=cache(k=None))
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, ca=cache(k=FAKE + 8))          # misaligned
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, ca=cache(capacity=1000))
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, red=None)
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, stride=1000)
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, lens=(1152, -1))
+    expect(B.RKV_ERR_UNSUPPORTED, gram, c, lens=(40000,), ca=cache(capacity=50000), stride=40000)
+    gram(c, lens=(1151, 9), red=None)   # nothing triggered: nothing enqueued
