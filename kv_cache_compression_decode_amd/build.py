@@ -30,6 +30,9 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# per-source additions: the Gram kernel scales every matrix-core result on
+# the vector ALUs, so its MFMAs write ordinary VGPRs (no copy out of AGPRs)
+EXTRA_FLAGS = {"rkv_gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd, verbose):
@@ -49,7 +52,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = OUT + ".tmp"

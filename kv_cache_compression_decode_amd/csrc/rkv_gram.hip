@@ -9,15 +9,18 @@
 // (exact operands; no rounding of normalised keys) and the two scalings are
 // applied in fp32:  R_j = (r_j * sum_i (k_j . k_i) r_i - r_j^2 |k_j|^2) / (N-1).
 //
-// A workgroup takes 128 rows of a unit (4 waves x 32 rows, held as MFMA A
-// operands in registers) and streams all of the unit's keys through LDS in
+// A workgroup takes 256 rows of a unit (4 waves x 64 rows, held as MFMA A
+// operands in registers; a wave whose rows all lie past N skips the
+// products) and streams all of the unit's keys through LDS in
 // double-buffered 64-key tiles.  Each 16 x 16 block of k_j . k_i is one chain
 // of v_mfma_f32_16x16x32_bf16 (fp32 accumulation) over the head dimension;
-// its entries are scaled by their column's r_i and summed into per-row
-// accumulators, so the matrix never leaves registers.  The column factors
-// r_i are computed while a tile is staged (the threads loading a key reduce
-// its squares across their lanes), so no pass over the keys precedes the
-// products and no workspace is needed.
+// the four row tiles' chains of one block run interleaved, and a block's
+// entries are scaled by their column's r_i (while the next block's chains
+// run) and summed into per-row accumulators, so the matrix never leaves
+// registers.  The column factors
+// r_i are computed while a tile is staged (the four threads loading a key
+// reduce its squares across their lanes), so no pass over the keys precedes
+// the products and no workspace is needed.
 //
 // Workgroups are mapped so that the row blocks of a unit run on one XCD
 // (workgroup b runs on XCD b % 8): the unit's keys are read from HBM into
@@ -33,24 +36,14 @@ namespace rkv {
 
 namespace {
 
-constexpr int kGramRows = 128;   // rows per workgroup: 4 waves x 32
+constexpr int kWaveRows = 64;                          // rows per wave: 4 MFMA row tiles
+constexpr int kRowTiles = kWaveRows / 16;
+constexpr int kGramRows = kWaveRows * kThreads / kWave;  // rows per workgroup
 constexpr int kGramTile = 64;    // keys per LDS tile
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes, a native vector
 
-// Sum over aligned groups of G consecutive lanes (G = 8 or 16); every lane of
-// the group gets it.
-template <int G>
-__device__ __forceinline__ float sum_lanes(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
-  if (G == 16)
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
-  return v;
-}
-
-__device__ __forceinline__ float sq8(const u32x4 w) {
-  float s = 0.f;
+// Sum of squares of the 8 bf16 values of a 16-byte piece (fp32, exact products).
+__device__ __forceinline__ float sq8(const u32x4 w, float s) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xFFFF0000u);
@@ -59,16 +52,24 @@ __device__ __forceinline__ float sq8(const u32x4 w) {
   return s;
 }
 
+// Sum over the aligned quad of lanes; every lane of the quad gets it.
+__device__ __forceinline__ float sum_quad(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  return v;
+}
+
 template <bool PAGED, int D>
 __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   constexpr int KS = D / 32;                             // MFMA k-steps over the head dimension
   constexpr int P = D + 8;                               // LDS row pitch (elements)
-  constexpr int TPK = D / 8;                             // threads per key when staging
-  constexpr int PPT = kGramTile * TPK / kThreads;        // 16-byte pieces per thread per tile
-  static_assert(kGramTile * TPK % kThreads == 0, "tile pieces spread evenly");
+  constexpr int QD = D / 4;                              // staging: 4 threads per key, QD dims each
+  constexpr int PPT = QD / 8;                            // 16-byte pieces per thread per tile
+  constexpr int CT = kGramTile / 16;                     // 16-key column blocks per tile
+  static_assert(kGramTile * 4 == kThreads, "one key per 4 threads when staging");
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGramTile * P];
   __shared__ float tinv[2][kGramTile];                  // r_i of the tile's keys
-  __shared__ float nrm2[kThreads / kWave][32];          // |k_j|^2 of each wave's rows
+  __shared__ float nrm2[kThreads / kWave][kWaveRows];   // |k_j|^2 of each wave's rows
 
   // work item of this workgroup: consecutive items (one unit's row blocks) on one XCD
   const int total = a.units * a.rblocks;
@@ -84,12 +85,13 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   const uint16_t* kc = static_cast<const uint16_t*>(a.k);
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, g4 = lane >> 4;
-  const int row0 = rb * kGramRows + wave * 32;
+  const int row0 = rb * kGramRows + wave * kWaveRows;
+  const bool live = row0 < n;   // wave-uniform
 
-  // this wave's 32 rows as A operands: row row0 + 16 rt + col, dims 32 ks + 8 g4 ..
-  bf16x8 af[2][KS];
+  // this wave's rows as A operands: row row0 + 16 rt + col, dims 32 ks + 8 g4 ..
+  bf16x8 af[kRowTiles][KS];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kRowTiles; ++rt) {
     const int r = row0 + 16 * rt + col;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -99,69 +101,79 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
     }
   }
 
-  // Tile loads: piece pc = t + i * kThreads is key pc / TPK of the tile, dims
-  // 8 (pc % TPK) ..; keys at or past n are zeros.
+  // Staging: thread t loads dims [QD sq, QD sq + QD) of key sk of the tile
+  // (keys at or past n are zeros), writes them to LDS and, with the other
+  // three threads of its key, the key's 1/|k|.
+  const int sk = t >> 2, sq = t & 3;
   const int ntiles = (n + kGramTile - 1) / kGramTile;
   u32x4 pre[PPT];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int pc = t + i * kThreads, key = pc / TPK;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < n) v = *reinterpret_cast<const u32x4*>(kc + rows.at(key) + 8 * (pc % TPK));
-    pre[i] = v;
+#define GRAM_LOAD(kt)                                                                          \
+  {                                                                                            \
+    const int key = (kt) * kGramTile + sk;                                                     \
+    const u32x4* src = reinterpret_cast<const u32x4*>(kc + rows.at(key < n ? key : 0) + QD * sq); \
+    _Pragma("unroll") for (int i = 0; i < PPT; ++i) pre[i] = key < n ? src[i] : u32x4{0u, 0u, 0u, 0u}; \
   }
-  // staged keys into LDS buffer b, with their column factors
 #define GRAM_STAGE(b)                                                                          \
-  _Pragma("unroll") for (int i = 0; i < PPT; ++i) {                                            \
-    const int pc = t + i * kThreads, key = pc / TPK;                                           \
-    *reinterpret_cast<u32x4*>(&tile[b][key * P + 8 * (pc % TPK)]) = pre[i];                    \
-    const float s = sum_lanes<TPK>(sq8(pre[i]));                                               \
-    if (pc % TPK == 0) tinv[b][key] = s > 0.f ? fast_rsqrt(s) : 0.f;                           \
+  {                                                                                            \
+    float ss = 0.f;                                                                            \
+    _Pragma("unroll") for (int i = 0; i < PPT; ++i) {                                          \
+      *reinterpret_cast<u32x4*>(&tile[b][sk * P + QD * sq + 8 * i]) = pre[i];                  \
+      ss = sq8(pre[i], ss);                                                                    \
+    }                                                                                          \
+    ss = sum_quad(ss);                                                                         \
+    if (sq == 0) tinv[b][sk] = ss > 0.f ? fast_rsqrt(ss) : 0.f;                                \
   }
+  GRAM_LOAD(0)
   GRAM_STAGE(0)
   lds_barrier();
 
-  float racc[2][4];
+  float racc[kRowTiles][4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) racc[rt][i] = 0.f;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < ntiles;
-    if (more) {   // the next tile's loads in flight during this tile's products
+    if (more) GRAM_LOAD(kt + 1)   // the next tile's loads in flight during this tile's products
+    if (live) {
+      // Block ct's four row-tile chains go into c[ct & 1] while block ct - 1's
+      // results are scaled by their columns' r_i and summed into the rows.
+      f32x4 c[2][kRowTiles];
+      float rcol[2];
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int pc = t + i * kThreads, key = (kt + 1) * kGramTile + pc / TPK;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (key < n) v = *reinterpret_cast<const u32x4*>(kc + rows.at(key) + 8 * (pc % TPK));
-        pre[i] = v;
-      }
-    }
+      for (int ct = 0; ct <= CT; ++ct) {
+        if (ct < CT) {
+          bf16x8 bf[KS];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      bf16x8 bf[KS];
+          for (int ks = 0; ks < KS; ++ks)
+            bf[ks] = *reinterpret_cast<const bf16x8*>(&tile[cur][(ct * 16 + col) * P + 32 * ks + 8 * g4]);
+          rcol[ct & 1] = tinv[cur][ct * 16 + col];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        bf[ks] = *reinterpret_cast<const bf16x8*>(&tile[cur][(ct * 16 + col) * P + 32 * ks + 8 * g4]);
-      const float ri = tinv[cur][ct * 16 + col];
+          for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < kRowTiles; ++rt)
+              c[ct & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  af[rt][ks], bf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : c[ct & 1][rt], 0, 0, 0);
+        }
+        if (ct > 0) {
+          const int pb = (ct - 1) & 1;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][ks], bf[ks], c, 0, 0, 0);
+          for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) racc[rt][i] = fmaf(c[i], ri, racc[rt][i]);
+            for (int i = 0; i < 4; ++i) racc[rt][i] = fmaf(c[pb][rt][i], rcol[pb], racc[rt][i]);
+        }
       }
     }
     if (more) GRAM_STAGE(cur ^ 1)
     lds_barrier();
   }
+#undef GRAM_LOAD
 #undef GRAM_STAGE
 
   // |k_j|^2 of row 16 rt + col, from the A operands (4 lanes per row)
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kRowTiles; ++rt) {
     float s = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   float* red = a.red + out_row(a.g, u) * a.stride;
   const float inv = 1.f / (float)(n - 1);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float s = sum_in_row(racc[rt][i]);
