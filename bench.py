@@ -338,6 +338,11 @@ def gram_bench(args, spec, case):
     ev[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
     ms = (t1 - t0) * 1e3 / steps
     us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
     flops = sum(2.0 * int(n) ** 2 * spec.head_dim for n in lens0[trig]) * spec.num_layers * spec.num_kv_heads
