@@ -133,6 +133,45 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def measured_peaks(torch, stream) -> dict:
+    """Achievable peaks measured on this GPU, next to the spec figures: a
+    1 GiB device-to-device copy (read + write bytes / time) for HBM, and an
+    8192^3 bf16 matrix product through torch (the vendor GEMM library) for
+    the matrix cores.  Best of five timed repetitions each."""
+    dev = torch.device("cuda:0")
+    out = {}
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    b.copy_(a)
+    best = None
+    for _ in range(5):
+        ev[0].record(stream)
+        b.copy_(a)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1]) * 1e-3
+        best = t if best is None else min(best, t)
+    out["hbm_copy_GBps"] = round(2 * a.numel() / best / 1e9, 1)
+    del a, b
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    z = torch.matmul(x, y)
+    best = None
+    for _ in range(5):
+        ev[0].record(stream)
+        torch.matmul(x, y, out=z)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1]) * 1e-3
+        best = t if best is None else min(best, t)
+    out["bf16_gemm_TFLOPs"] = round(2.0 * n ** 3 / best / 1e12, 1)
+    del x, y, z
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -262,6 +301,9 @@ def main():
     tb = measured_traffic(dom, spec.name)
     if tb is not None:
         roofline["traffic"] = tb
+    peaks = measured_peaks(torch, stream)
+    roofline["peak_measured"] = peaks["hbm_copy_GBps"]
+    roofline["frac_measured"] = round(achieved / peaks["hbm_copy_GBps"], 4)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -295,6 +337,7 @@ def main():
         "kernel_timing": ("HIP events around each kernel" if args.three_calls else
                           "HIP events around the timed region / steps (one kernel per step)"),
         "moved_rows": moved_rows,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -347,6 +390,7 @@ def gram_bench(args, spec, case):
     us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
     flops = sum(2.0 * int(n) ** 2 * spec.head_dim for n in lens0[trig]) * spec.num_layers * spec.num_kv_heads
     tflops = flops / (us * 1e-6) / 1e12
+    peaks = measured_peaks(torch, stream)
     out = {
         "metric": "Gram redundancy passes/sec (every triggered unit's N x N cosine matrix); % MFMA roofline",
         "value": round(1e6 / us, 2),
@@ -368,7 +412,9 @@ def gram_bench(args, spec, case):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("gram", spec.name), "kernel": "gram",
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops, "peak_measured": peaks["bf16_gemm_TFLOPs"],
+                     "frac_measured": round(tflops / peaks["bf16_gemm_TFLOPs"], 4)},
+        "measured_peaks": peaks,
         "kernels": {"gram": {"us": round(us, 2)}},
         "kernel_timing": "HIP events around the timed region / steps (one kernel per launch)",
         "cpu_baseline": None,
