@@ -68,14 +68,14 @@ def check_untriggered_rows(case, red):
 
 
 CASES = {
-    # several 128-row blocks and 64-key tiles, ragged tails, one sequence below the trigger
+    # several 256-row blocks and 64-key tiles, ragged tails, one sequence below the trigger
     "ragged-d128": syn.config(1).with_(name="g-ragged", seed=41, num_seqs=3, num_layers=2,
                                         num_q_heads=8, num_kv_heads=2, budget=256, buffer=32,
                                         lens=(777, 250, 300)),
     "d64-mha": syn.config(1).with_(name="g-d64", seed=42, num_seqs=2, num_layers=2, num_q_heads=4,
                                     num_kv_heads=4, head_dim=64, window=4, budget=200, buffer=40,
                                     lens=(513, 240)),
-    # shortest trigger: N = 2 .. a handful of keys, one partial tile
+    # short units: N = 3 (the shortest this budget triggers), one partial tile, one row block
     "tiny-units": syn.config(1).with_(name="g-tiny", seed=43, num_seqs=3, num_layers=1,
                                        num_q_heads=2, num_kv_heads=2, window=1, budget=2, buffer=1,
                                        lens=(3, 65, 129)),
@@ -159,3 +159,21 @@ def test_gram_max_length():
     got = red[0].cpu().numpy()
     assert np.all(np.isfinite(got)), "every row of the unit written"
     log(f"gram max length: N={n} sampled rows match the oracle (max error {err:.2e})")
+
+
+def test_gram_many_sequences():
+    """More triggered sequences than one launch's table holds (128): the call
+    runs several launches; sequences of the second launch and untriggered
+    ones in between are checked."""
+    lens = tuple(70 if s % 7 else 50 for s in range(160))    # every 7th below the trigger
+    spec = syn.config(1).with_(name="g-many", seed=50, num_seqs=160, num_layers=1, num_q_heads=2,
+                               num_kv_heads=1, head_dim=64, window=2, budget=60, buffer=10,
+                               lens=lens)
+    case = ContigCase(spec)
+    red = run_gram(case)
+    trig = [s for s in range(spec.num_seqs) if lens[s] >= spec.budget + spec.buffer]
+    assert len(trig) > 128
+    for s in trig[:3] + trig[125:]:
+        check_gram_unit(case, red, s, 0, 0)
+    check_untriggered_rows(case, red)
+    log(f"gram many sequences: {len(trig)} triggered, launches split at 128, sampled units match")
