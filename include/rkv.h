@@ -26,6 +26,15 @@
  *     the call only.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     is asynchronous: results are valid once the stream reaches that point.
+ *   - bf16 units longer than one workgroup holds (more than 1280 keys at
+ *     head_dim 128, 2560 at 64) are scored by several workgroups that wait
+ *     for one another (rkv_score, and rkv_step / rkv_step_device when they
+ *     fall back to the three kernels).  Each launch only takes as many
+ *     workgroups as the device holds at once, but two such launches running
+ *     at the same time on different streams of one device can hold each
+ *     other's room: run such calls on one stream (or one at a time).  The
+ *     wait is bounded (one second), so the device never hangs; a wait that
+ *     reaches the bound leaves that launch's scores wrong.
  *   - Every argument is checked before anything is enqueued.  On an error the
  *     call returns a status other than RKV_OK, enqueues nothing and changes no
  *     output; rkv_last_error() then describes it.  No C++ exception crosses

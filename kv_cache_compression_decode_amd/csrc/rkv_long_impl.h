@@ -21,6 +21,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 
 #include "rkv_unit_impl.h"
 
@@ -132,13 +133,15 @@ __global__ __launch_bounds__(kUnitThreads) void score_long_kernel(ScoreArgs a, L
 
 template <bool PAGED, int D, int RT>
 hipError_t launch_long_t(const ScoreArgs& a, int chunks, hipStream_t st) {
-  // resident workgroups: per device, computed once
-  static int grid_of[64] = {0};
+  // resident workgroups: per device, computed once (atomic: calls may come
+  // from several host threads; a repeated computation stores the same value)
+  static std::atomic<int> grid_of[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (grid_of[dev] == 0) {
+  int resident = grid_of[dev].load(std::memory_order_relaxed);
+  if (resident == 0) {
     int cus = 0, occ = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return e;
@@ -147,9 +150,10 @@ hipError_t launch_long_t(const ScoreArgs& a, int chunks, hipStream_t st) {
         hipSuccess)
       return e;
     if (cus <= 0 || occ <= 0) return hipErrorInvalidConfiguration;
-    grid_of[dev] = cus * occ;
+    resident = cus * occ;
+    grid_of[dev].store(resident, std::memory_order_relaxed);
   }
-  const int per = grid_of[dev] / chunks;   // units whose spans are all resident at once
+  const int per = resident / chunks;   // units whose spans are all resident at once
   if (per < 1) return hipErrorInvalidConfiguration;
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
   hipLaunchKernelGGL(long_zero_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a, chunks, units);
