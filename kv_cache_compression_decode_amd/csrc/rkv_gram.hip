@@ -59,6 +59,34 @@ __device__ __forceinline__ float sum_quad(float v) {
   return v;
 }
 
+// Staging of a 64-key tile: thread (sk, sq) loads dims [QD sq, QD sq + QD) of
+// key sk of tile kt (keys at or past n are zeros) ...
+template <bool PAGED, int D>
+__device__ __forceinline__ void gram_load(u32x4 (&pre)[D / 32], const uint16_t* kc, const KeyRows<PAGED>& rows,
+                                          int kt, int n, int sk, int sq) {
+  constexpr int QD = D / 4, PPT = D / 32;
+  const int key = kt * kGramTile + sk;
+  const u32x4* src = reinterpret_cast<const u32x4*>(kc + rows.at(key < n ? key : 0) + QD * sq);
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) pre[i] = key < n ? src[i] : u32x4{0u, 0u, 0u, 0u};
+}
+
+// ... then writes them to the LDS tile (row pitch D + 8) and, with the other
+// three threads of its key, the key's 1/|k| (0 for a zero key).
+template <int D>
+__device__ __forceinline__ void gram_stage(const u32x4 (&pre)[D / 32], uint16_t* tile, float* tinv, int sk,
+                                           int sq) {
+  constexpr int QD = D / 4, PPT = D / 32, P = D + 8;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    *reinterpret_cast<u32x4*>(&tile[sk * P + QD * sq + 8 * i]) = pre[i];
+    ss = sq8(pre[i], ss);
+  }
+  ss = sum_quad(ss);
+  if (sq == 0) tinv[sk] = ss > 0.f ? fast_rsqrt(ss) : 0.f;
+}
+
 template <bool PAGED, int D>
 __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   constexpr int KS = D / 32;                             // MFMA k-steps over the head dimension
@@ -101,30 +129,12 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
     }
   }
 
-  // Staging: thread t loads dims [QD sq, QD sq + QD) of key sk of the tile
-  // (keys at or past n are zeros), writes them to LDS and, with the other
-  // three threads of its key, the key's 1/|k|.
+  // staging: four threads per key
   const int sk = t >> 2, sq = t & 3;
   const int ntiles = (n + kGramTile - 1) / kGramTile;
   u32x4 pre[PPT];
-#define GRAM_LOAD(kt)                                                                          \
-  {                                                                                            \
-    const int key = (kt) * kGramTile + sk;                                                     \
-    const u32x4* src = reinterpret_cast<const u32x4*>(kc + rows.at(key < n ? key : 0) + QD * sq); \
-    _Pragma("unroll") for (int i = 0; i < PPT; ++i) pre[i] = key < n ? src[i] : u32x4{0u, 0u, 0u, 0u}; \
-  }
-#define GRAM_STAGE(b)                                                                          \
-  {                                                                                            \
-    float ss = 0.f;                                                                            \
-    _Pragma("unroll") for (int i = 0; i < PPT; ++i) {                                          \
-      *reinterpret_cast<u32x4*>(&tile[b][sk * P + QD * sq + 8 * i]) = pre[i];                  \
-      ss = sq8(pre[i], ss);                                                                    \
-    }                                                                                          \
-    ss = sum_quad(ss);                                                                         \
-    if (sq == 0) tinv[b][sk] = ss > 0.f ? fast_rsqrt(ss) : 0.f;                                \
-  }
-  GRAM_LOAD(0)
-  GRAM_STAGE(0)
+  gram_load<PAGED, D>(pre, kc, rows, 0, n, sk, sq);
+  gram_stage<D>(pre, &tile[0][0], tinv[0], sk, sq);
   lds_barrier();
 
   float racc[kRowTiles][4];
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < ntiles;
-    if (more) GRAM_LOAD(kt + 1)   // the next tile's loads in flight during this tile's products
+    if (more) gram_load<PAGED, D>(pre, kc, rows, kt + 1, n, sk, sq);   // in flight during the products
     if (live) {
       // Block ct's four row-tile chains go into c[ct & 1] while block ct - 1's
       // results are scaled by their columns' r_i and summed into the rows.
@@ -165,11 +175,9 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
         }
       }
     }
-    if (more) GRAM_STAGE(cur ^ 1)
+    if (more) gram_stage<D>(pre, &tile[cur ^ 1][0], tinv[cur ^ 1], sk, sq);
     lds_barrier();
   }
-#undef GRAM_LOAD
-#undef GRAM_STAGE
 
   // |k_j|^2 of row 16 rt + col, from the A operands (4 lanes per row)
 #pragma unroll
