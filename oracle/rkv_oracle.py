@@ -36,6 +36,7 @@ __all__ = [
     "redundancy", "mixed_score", "score_unit", "select_keep", "compact_rows",
     "free_blocks", "unit_step", "q_group", "step_contiguous", "step_unit",
     "shared_score", "select_keep_shared", "layer_step_shared", "redundancy_at",
+    "window_store",
 ]
 
 
@@ -200,6 +201,22 @@ def layer_step_shared(q_rows_per_head, k_per_head, k_store, v_store, budget, win
     return [dict(imp=imp, red=red, score=sc, keep=keep,
                  k_new=compact_rows(ks, keep), v_new=compact_rows(vs, keep))
             for (imp, red, sc), ks, vs in zip(heads, k_store, v_store)]
+
+
+def window_store(q_window: np.ndarray, q_step: np.ndarray, layer0: int, steps, window: int) -> np.ndarray:
+    """[PROJ] "How R-KV decides what to drop": the last window_size queries of
+    a sequence score its cache.  Reading: they are kept in a ring of `window`
+    slots per (layer, sequence, query head); decode step t of sequence s
+    writes its query into slot t mod window, so after any window consecutive
+    steps the ring holds exactly the last window queries (in rotated order,
+    which importance() does not see: it averages over the rows).
+    q_window (L, S, Hq, w, d), q_step (count, S, Hq, d) for layers
+    layer0 .. layer0 + count - 1; returns the updated copy (a bit copy)."""
+    out = np.array(q_window, copy=True)
+    for i in range(q_step.shape[0]):
+        for s in range(q_step.shape[1]):
+            out[layer0 + i, s, :, int(steps[s]) % window, :] = q_step[i, s]
+    return out
 
 
 def q_group(q_seq_layer: np.ndarray, h: int, group: int) -> np.ndarray:

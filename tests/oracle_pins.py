@@ -369,6 +369,41 @@ def pin_shared_layer_step(o):
         _close(res[h]["k_new"], ks[h][np.array(total)])
 
 
+def pin_window_ring_holds_last_queries(o):
+    """After any window consecutive decode steps the ring holds exactly the
+    last window queries, query t in slot t mod window; layers outside the
+    call are untouched."""
+    rng = np.random.default_rng([77, 90])
+    L, S, Hq, w, d = 3, 3, 2, 4, 3
+    start = [0, 5, 13]
+    ring = np.full((L, S, Hq, w, d), -1.0)
+    history = []
+    for t in range(7):
+        q = rng.standard_normal((2, S, Hq, d))
+        steps = [s0 + t for s0 in start]
+        ring = o.window_store(ring, q, 1, steps, w)
+        history.append((steps, q))
+    assert np.all(ring[0] == -1.0), "layer 0 was not part of the calls"
+    for s in range(S):
+        for h in range(Hq):
+            for li in range(2):
+                want = {tuple(q[li, s, h]) for _, q in history[-w:]}
+                got = {tuple(ring[1 + li, s, h, j]) for j in range(w)}
+                assert got == want
+            for steps, q in history[-w:]:
+                assert np.array_equal(ring[1:, s, h, steps[s] % w], q[:, s, h])
+
+
+def pin_importance_ignores_window_row_order(o):
+    """The ring keeps the window queries in rotated order; importance is a
+    mean over the rows, so any order of them gives the same result."""
+    q, k = _rand_case(91, 40, 8, 12)
+    perm = np.random.default_rng([77, 91]).permutation(q.shape[0])
+    _close(o.importance(q[perm], k), o.importance(q, k), tol=1e-13)
+    roll = np.roll(q.reshape(3, 4, 8), 1, axis=1).reshape(12, 8)   # a rotated ring per head
+    _close(o.importance(roll, k), o.importance(q, k), tol=1e-13)
+
+
 def pin_page_defaults(o):
     """The workloads use the pages' default knobs."""
     import rkv_synth as syn

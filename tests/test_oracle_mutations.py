@@ -50,6 +50,12 @@ MUTANTS = [
     ("shared: max over heads", "return hs.sum(axis=0)", "return hs.max(axis=0)"),
     ("shared: first head only", "return hs.sum(axis=0)", "return hs[0]"),
     ("shared: mean over heads", "return hs.sum(axis=0)", "return hs.mean(axis=0)"),
+    ("ring slot t // window", "out[layer0 + i, s, :, int(steps[s]) % window, :] = q_step[i, s]",
+     "out[layer0 + i, s, :, (int(steps[s]) // window) % window, :] = q_step[i, s]"),
+    ("ring ignores layer0", "out[layer0 + i, s, :, int(steps[s]) % window, :] = q_step[i, s]",
+     "out[i, s, :, int(steps[s]) % window, :] = q_step[i, s]"),
+    ("ring slot shifted by one", "out[layer0 + i, s, :, int(steps[s]) % window, :] = q_step[i, s]",
+     "out[layer0 + i, s, :, (int(steps[s]) + 1) % window, :] = q_step[i, s]"),
     ("shared layer: per-head keep", "keep = select_keep_shared(np.stack([h[2] for h in heads]), n, budget, window)",
      "keep = select_keep(heads[0][2], n, budget, window)"),
 ]
