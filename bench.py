@@ -54,6 +54,8 @@ def parse():
                    help="head-shared selection (one keep set per sequence and layer; three kernels)")
     p.add_argument("--gram", action="store_true",
                    help="time rkv_redundancy_gram (the explicit cosine Gram on the matrix cores) instead")
+    p.add_argument("--window-store", action="store_true",
+                   help="time rkv_window_store (one decode step's queries, all layers, into the ring)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed region, one 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -190,6 +192,8 @@ def main():
     spec = syn.config(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.window_store:
+        return window_store_bench(args, spec)
     case = PagedCase(spec) if spec.layout == "paged" else ContigCase(spec)
     if args.gram:
         return gram_bench(args, spec, case)
@@ -371,6 +375,62 @@ def main():
         "moved_rows": moved_rows,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def window_store_bench(args, spec):
+    """rkv_window_store for one decode step of the workload's batch: every
+    layer's queries (num_seqs x num_q_heads rows of head_dim) into the ring,
+    one call.  Algorithmic bytes: the rows read once and written once."""
+    import numpy as np
+    import torch
+
+    from gpu_harness import config_of
+    from kv_cache_compression_decode_amd import binding as B
+
+    steps = 100 if args.steps is None else args.steps
+    cfg = config_of(spec)
+    dt = torch.int16 if spec.dtype == "bf16" else torch.float32
+    L, S, H, d, w = spec.num_layers, spec.num_seqs, spec.num_q_heads, spec.head_dim, spec.window
+    q = torch.randn((L, S, H, d), device="cuda").to(dt) if dt == torch.float32 else \
+        torch.randint(-2000, 2000, (L, S, H, d), dtype=dt, device="cuda")
+    ring = torch.zeros((L, S, H, w, d), dtype=dt, device="cuda")
+    ctr = torch.arange(S, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        B.rkv_window_store(cfg, 0, L, q, S, ctr, ring, stream)
+
+    for _ in range(args.warmup):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(steps):
+        run()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    nbytes = 2 * q.numel() * q.element_size()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out = {
+        "metric": "window-query ring stores/sec (one decode step's queries, all layers)",
+        "value": round(1e6 / us, 2), "unit": "stores/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round((t1 - t0) * 1e3 / steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "num_layers": L, "num_seqs": S, "num_q_heads": H,
+                   "head_dim": d, "window": w},
+        "entry": "rkv_window_store",
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "window_store",
+                     "bytes_per_launch": nbytes},
+        "kernels": {"window_store": {"us": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1)}},
+        "kernel_timing": "HIP events around the timed region / launches (one kernel per launch)",
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

@@ -149,6 +149,29 @@ rkv_status rkv_score(const rkv_config *cfg, const rkv_cache *cache, const void *
                      float *importance, float *redundancy,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* The window-query ring of the decode loop: the last `window` queries of each
+ * sequence, which the scoring calls read as q_window ("How R-KV decides what
+ * to drop": the last window_size queries score the cache).  Decode step t of
+ * sequence s stores its queries (every query head) into slot t mod window of
+ * q_window, for layers layer0 .. layer0 + layer_count - 1; after any window
+ * consecutive steps the ring holds exactly the last window queries.  The
+ * scoring averages over the window rows, so their rotated order does not
+ * change any result beyond float rounding.  The slot is computed on the GPU,
+ * so the call can be captured in a decode graph.
+ *   q_step    device, the step's queries [layer_count][num_seqs][num_q_heads][head_dim]
+ *             in the cache dtype, 16-byte aligned
+ *   d_steps   device int32 [num_seqs]: each sequence's decode step counter
+ *             (any integer; a counter that keeps counting across compaction,
+ *             unlike the cache length, which drops to `budget`)
+ *   q_window  device, [num_layers][num_seqs][num_q_heads][window][head_dim]
+ *             (the layout of rkv_score's q_window), 16-byte aligned; only the
+ *             slot of each (layer, sequence, head) is written
+ * Errors: RKV_ERR_INVALID_ARG (NULL, misaligned, layers outside
+ * [0, num_layers)), RKV_ERR_UNSUPPORTED (as for the config), RKV_ERR_HIP. */
+rkv_status rkv_window_store(const rkv_config *cfg, int32_t layer0, int32_t layer_count,
+                            const void *q_step, int32_t num_seqs, const int32_t *d_steps,
+                            void *q_window, void *stream);
+
 /* The redundancy signal alone, through the explicit cosine Gram matrix: for
  * every key j of every triggered unit, R_j = the mean of cos(k_j, k_i) over
  * the unit's other keys i, with cos = 0 against a zero key -- the mean

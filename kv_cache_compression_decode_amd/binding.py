@@ -32,7 +32,7 @@ RKV_MAX_WINDOW_ROWS = 142
 
 # Every function declared in include/rkv.h.
 EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_workspace_size",
-           "rkv_redundancy_gram",
+           "rkv_redundancy_gram", "rkv_window_store",
            "rkv_score", "rkv_select", "rkv_compact", "rkv_step",
            "rkv_step_device_workspace_size", "rkv_step_device")
 
@@ -84,6 +84,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rkv_redundancy_gram.argtypes = [P(rkv_config), P(rkv_cache), c_int32, P(c_int32),
                                         c_void_p, c_int32, c_void_p]
     lib.rkv_redundancy_gram.restype = c_int32
+    lib.rkv_window_store.argtypes = [P(rkv_config), c_int32, c_int32, c_void_p, c_int32, c_void_p,
+                                     c_void_p, c_void_p]
+    lib.rkv_window_store.restype = c_int32
     lib.rkv_select.argtypes = [P(rkv_config), c_int32, P(c_int32), c_void_p, c_int32, c_void_p,
                                c_void_p]
     lib.rkv_select.restype = c_int32
@@ -173,6 +176,13 @@ def rkv_score(cfg, cache, q_window, num_seqs, seq_lens, scores, score_stride,
     _check(load().rkv_score(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q_window), num_seqs,
                             _i32p(lens), _ptr(scores), score_stride, _ptr(importance),
                             _ptr(redundancy), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def rkv_window_store(cfg, layer0, layer_count, q_step, num_seqs, d_steps, q_window,
+                     stream=None) -> None:
+    """d_steps: device int32 [num_seqs] (torch tensor or address)."""
+    _check(load().rkv_window_store(ctypes.byref(cfg), layer0, layer_count, _ptr(q_step), num_seqs,
+                                   _ptr(d_steps), _ptr(q_window), _stream(stream)))
 
 
 def rkv_redundancy_gram(cfg, cache, num_seqs, seq_lens, redundancy, stride, stream=None) -> None:

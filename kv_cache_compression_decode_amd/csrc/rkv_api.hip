@@ -303,6 +303,40 @@ rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* 
   return RKV_OK;
 }
 
+rkv_status rkv_window_store(const rkv_config* cfg, int32_t layer0, int32_t layer_count,
+                            const void* q_step, int32_t num_seqs, const int32_t* d_steps,
+                            void* q_window, void* stream) {
+  g_err.clear();
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  if (num_seqs < 0) return fail(RKV_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (layer0 < 0 || layer_count < 0 || (int64_t)layer0 + layer_count > cfg->num_layers)
+    return fail(RKV_ERR_INVALID_ARG, "layers [%d, %d + %d) are outside [0, %d)", layer0, layer0,
+                layer_count, cfg->num_layers);
+  if (num_seqs == 0 || layer_count == 0) return RKV_OK;
+  if (q_step == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_step is NULL");
+  if (d_steps == nullptr) return fail(RKV_ERR_INVALID_ARG, "d_steps is NULL");
+  if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
+  if (!aligned16(q_step) || !aligned16(q_window))
+    return fail(RKV_ERR_INVALID_ARG, "q_step and q_window must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(d_steps) & 3u) != 0)
+    return fail(RKV_ERR_INVALID_ARG, "d_steps must be 4-byte aligned");
+  rkv::WindowArgs a{};
+  a.q_step = static_cast<const uint8_t*>(q_step);
+  a.q_window = static_cast<uint8_t*>(q_window);
+  a.steps = d_steps;
+  a.layer0 = layer0;
+  a.count = layer_count;
+  a.num_seqs = num_seqs;
+  a.hq = cfg->num_q_heads;
+  a.window = cfg->window;
+  a.row_bytes = cfg->head_dim * (cfg->dtype == RKV_DTYPE_BF16 ? 2 : 4);
+  a.pieces = (int64_t)layer_count * num_seqs * cfg->num_q_heads * (a.row_bytes / 16);
+  const hipError_t e = rkv::launch_window_store(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "window store launch");
+  return RKV_OK;
+}
+
 rkv_status rkv_redundancy_gram(const rkv_config* cfg, const rkv_cache* cache, int32_t num_seqs,
                                const int32_t* h_seq_lens, float* redundancy, int32_t stride,
                                void* stream) {

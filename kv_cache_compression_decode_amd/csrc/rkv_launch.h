@@ -79,6 +79,16 @@ struct GramArgs {
   int32_t rblocks;        // 128-row blocks per unit: gram_row_blocks(longest length)
 };
 
+// Window-query ring store (rkv_window_store).
+struct WindowArgs {
+  const uint8_t* q_step;    // [count][num_seqs][hq][row_bytes]
+  uint8_t* q_window;        // [L][num_seqs][hq][window][row_bytes]
+  const int32_t* steps;     // device [num_seqs]: decode step of each sequence
+  int32_t layer0, count, num_seqs, hq, window, row_bytes;
+  int64_t pieces;           // 16-byte pieces to copy: count * num_seqs * hq * row_bytes / 16
+};
+
+hipError_t launch_window_store(const WindowArgs& a, hipStream_t st);
 hipError_t launch_table(const TableArgs& a, hipStream_t st);
 int gram_row_blocks(int max_len);
 hipError_t launch_gram(const GramArgs& a, hipStream_t st);

@@ -231,3 +231,24 @@ def test_gram_argument_errors():
     expect(B.RKV_ERR_INVALID_ARG, gram, c, lens=(1152, -1))
     expect(B.RKV_ERR_UNSUPPORTED, gram, c, lens=(40000,), ca=cache(capacity=50000), stride=40000)
     gram(c, lens=(1151, 9), red=None)   # nothing triggered: nothing enqueued
+
+
+def wstore(c, layer0=0, count=32, q=FAKE, n=1, steps=FAKE, ring=FAKE * 4):
+    B.rkv_window_store(c, layer0, count, q, n, steps, ring, None)
+
+
+def test_window_store_argument_errors():
+    c = cfg()
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, layer0=-1)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, layer0=1, count=32)      # past the last layer
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, count=-1)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, n=-1)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, q=None)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, steps=None)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, ring=None)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, q=FAKE + 8)              # misaligned
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, ring=FAKE * 4 + 8)
+    expect(B.RKV_ERR_INVALID_ARG, wstore, c, steps=FAKE + 2)
+    expect(B.RKV_ERR_UNSUPPORTED, wstore, cfg(head_dim=96))
+    wstore(c, n=0, q=None, steps=None, ring=None)                     # nothing to store
+    wstore(c, count=0, q=None, steps=None, ring=None)
