@@ -13,10 +13,15 @@ from kv_cache_compression_decode_amd.step import RKVStep
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("which", ["llama8b-1seq", "paged-small"])
+@pytest.mark.parametrize("which", ["llama8b-1seq", "paged-small", "spans"])
 def test_graph_replays_match_eager(which):
     if which == "llama8b-1seq":
         spec = syn.config(1)
+        case = ContigCase(spec)
+    elif which == "spans":   # units longer than one workgroup: key-span launches + counter reset
+        spec = syn.config(1).with_(name="gspan", seed=51, num_seqs=2, num_layers=2, num_q_heads=4,
+                                   num_kv_heads=2, head_dim=64, budget=2000, buffer=100,
+                                   lens=(3100, 1500))
         case = ContigCase(spec)
     else:
         spec = syn.config(3).with_(name="pg", seed=50, num_seqs=3, num_layers=2, budget=500,
