@@ -126,6 +126,14 @@ SMALL = {
     "spans-d64": syn.config(1).with_(name="spd", seed=27, num_seqs=1, num_layers=2, num_q_heads=4,
                                      num_kv_heads=2, head_dim=64, budget=2000, buffer=100,
                                      lens=(3100,)),
+    # key spans over a paged cache at head_dim 64 (units above 2560 keys)
+    "spans-paged-d64": syn.config(3).with_(name="spp", seed=28, num_seqs=2, num_layers=2,
+                                           num_q_heads=4, num_kv_heads=2, head_dim=64, budget=2600,
+                                           buffer=100, num_blocks=500, lens=(2750, 3300)),
+    # fp32 caches in the paged layout
+    "f32-paged": syn.config(3).with_(name="f32p", seed=29, dtype="f32", num_seqs=2, num_layers=2,
+                                     num_q_heads=8, num_kv_heads=2, budget=300, buffer=40,
+                                     num_blocks=100, lens=(345, 500)),
 }
 
 
