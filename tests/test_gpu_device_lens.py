@@ -21,6 +21,10 @@ CASES = {
                                        num_blocks=400, lens=(345, 1280, 200)), False),
     "long-2176": (syn.config(2).with_(num_seqs=2, num_layers=2, len_range=None,
                                       lens=(2176, 2100)), False),
+    # paged units long enough for key spans, one sequence below the trigger
+    "paged-spans": (syn.config(3).with_(name="dl-ps", seed=84, num_seqs=3, num_layers=2,
+                                        num_q_heads=8, num_kv_heads=2, budget=1200, buffer=100,
+                                        num_blocks=600, lens=(1400, 3000, 900)), False),
     "f32-tiny": (syn.config(0), False),
     "shared-ragged": (syn.config(1).with_(name="dl-s", seed=83, num_seqs=3, num_layers=2,
                                           num_q_heads=8, num_kv_heads=2, budget=256, buffer=32,
