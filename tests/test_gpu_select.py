@@ -68,3 +68,20 @@ def test_select_longest_cache():
         s = scores_for(kind, n, rng)
         got = run_select(s, n, 1024, n - 1024, 8)
         assert np.array_equal(got, O.select_keep(s.astype(np.float64), n, 1024, 8)), kind
+
+
+@pytest.mark.parametrize("frac", [0.1, 1.0])
+@pytest.mark.parametrize("n,budget,buffer", [(1152, 1024, 128), (200, 20, 180), (4352, 4096, 256)])
+def test_select_nan_scores_give_a_valid_set(frac, n, budget, buffer):
+    """NaN scores: the set is unspecified, but it must be a valid keep row --
+    budget entries, strictly ascending, in range, the window at the end."""
+    rng = np.random.default_rng([int(frac * 10), n])
+    s = rng.normal(0, 1, n).astype(F32)
+    s[rng.choice(n, int(frac * n), replace=False)] = np.nan
+    w = 8
+    got = run_select(s, n, budget, buffer, w)
+    assert got.shape == (budget,)
+    assert np.all(np.diff(got) > 0), "not strictly ascending"
+    assert got[0] >= 0 and got[-1] == n - 1
+    assert np.array_equal(got[budget - w:], np.arange(n - w, n)), "window not kept"
+    assert np.all(got[: budget - w] < n - w)
