@@ -110,19 +110,31 @@ def cpu_baseline(spec, case, seconds: float):
     units = [(s, l, h) for s in range(spec.num_seqs) for l in range(spec.num_layers)
              for h in range(spec.num_kv_heads)
              if case.lens0[s] >= spec.budget + spec.buffer]
-    done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        s, l, h = units[done % len(units)]
-        kr, vr = case.unit_rows(s, l, h)
-        O.step_unit(spec, case.q_host[l, s], kr, vr, h)
-        done += 1
-    dt = time.perf_counter() - t0
+    def sample(budget):
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            s, l, h = units[done % len(units)]
+            kr, vr = case.unit_rows(s, l, h)
+            O.step_unit(spec, case.q_host[l, s], kr, vr, h)
+            done += 1
+        return done, time.perf_counter() - t0
+
+    done, dt = sample(seconds)
     steps_per_s = done / dt / len(units)
-    return {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "cpu": cpu_model(),
-            "sample": f"{done} of the step's {len(units)} units (float64 numpy, explicit N x N "
-                      f"Gram), {dt:.1f} s; value = units/s / units per step"}
+    out = {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
+           "cpu": cpu_model(),
+           "sample": f"{done} of the step's {len(units)} units (float64 numpy, explicit N x N "
+                     f"Gram), {dt:.1f} s; value = units/s / units per step"}
+    try:   # the same oracle on one thread, a third of the time budget
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, t1 = sample(seconds / 3)
+        out["value_1thread"] = round(d1 / t1 / len(units), 4)
+        out["sample_1thread"] = f"{d1} units, {t1:.1f} s, one BLAS thread"
+    except Exception:  # noqa: BLE001 - the single-thread figure is optional context
+        pass
+    return out
 
 
 def cpu_model() -> str:
