@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librkv.so")
+EXAMPLE = os.path.join(PKG, "rkv_c_example")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -57,9 +58,13 @@ def build(verbose: bool = False) -> str:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = OUT + ".tmp"
     # --no-undefined: a kernel the compiler dropped shows up here, not at load time
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp],
-         verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined",
+          "-Wl,-soname,librkv.so", *objs, "-o", tmp], verbose)
     os.replace(tmp, OUT)
+    # a caller of the C ABI without Python (run by the GPU tests), linked against
+    # the library next to it
+    _run([HIPCC, *FLAGS, os.path.join(PKG, "examples", "rkv_c_example.cpp"), f"-L{PKG}", "-lrkv",
+          "-Wl,-rpath,$ORIGIN", "-o", EXAMPLE], verbose)
     return OUT
 
 
