@@ -1,0 +1,75 @@
+"""Seeded random configurations across the supported space -- dtype, layout
+and block size, head_dim, GQA group, window, budget and buffer, lambda,
+head-shared selection, ragged lengths on both sides of the trigger -- each
+run through the three calls and checked against the oracle on sampled units,
+and through rkv_step, which must give the same bytes."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import rkv_synth as syn
+from gpu_harness import check_layer_shared, check_unit, log, make_case, run_step, sample_units
+
+pytestmark = pytest.mark.gpu
+
+DRAWS = 32
+
+
+def random_spec(i):
+    rng = np.random.default_rng([2024, i])
+    dtype = "bf16" if rng.random() < 0.8 else "f32"
+    paged = rng.random() < 0.4
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    w = int(rng.choice([1, 2, 4, 8, 16]))
+    g = int(rng.choice([x for x in (1, 2, 4, 7, 8) if x * w <= 142]))
+    budget = int(rng.integers(w + 1, 600))
+    buffer = int(rng.integers(1, 200))
+    trig = budget + buffer
+    S = int(rng.integers(1, 5))
+    lens = tuple(int(rng.integers(max(1, trig // 2), trig)) if rng.random() < 0.25
+                 else int(rng.integers(trig, trig + 1300)) for _ in range(S))
+    bs = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256]))
+    spec = syn.Spec(name=f"rand{i}", seed=3000 + i, num_seqs=S, num_layers=int(rng.integers(1, 4)),
+                    num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, dtype=dtype, budget=budget,
+                    buffer=buffer, window=w, mix_lambda=float(rng.choice([0.0, 0.1, 0.5, 1.0])),
+                    layout="paged" if paged else "contiguous", block_size=bs,
+                    num_blocks=S * math.ceil(max(lens) / bs) + 7, lens=lens,
+                    key_mean_std=0.5, dup_mode="scatter", dup_frac=0.2)
+    return spec, bool(rng.random() < 0.2)
+
+
+def as_bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+@pytest.mark.parametrize("i", range(DRAWS))
+def test_random_configuration(i):
+    spec, shared = random_spec(i)
+    desc = (f"{spec.dtype} {spec.layout} bs{spec.block_size} d{spec.head_dim} G{spec.group} "
+            f"w{spec.window} B{spec.budget}+{spec.buffer} lam{spec.mix_lambda} "
+            f"lens{spec.lens} L{spec.num_layers} Hkv{spec.num_kv_heads} shared={shared}")
+    log(f"draw {i}: {desc}")
+    case = make_case(spec)
+    step, lens = run_step(case, shared=shared)
+    trig = [s for s in range(spec.num_seqs) if spec.lens[s] >= spec.budget + spec.buffer]
+    want = np.array([spec.budget if s in trig else spec.lens[s] for s in range(spec.num_seqs)])
+    assert np.array_equal(lens, want), f"draw {i}: lengths {lens} vs {want}"
+    units = sample_units(spec, 24, seed=i)
+    if shared:
+        for s, l in sorted({(s, l) for s, l, _ in units}):
+            check_layer_shared(case, step, s, l, f"rand{i}")
+    else:
+        for s, l, h in units:
+            check_unit(case, step, s, l, h, f"rand{i}")
+    # rkv_step on a fresh copy of the same inputs: the same bytes
+    case2 = make_case(spec)
+    step2, lens2 = run_step(case2, shared=shared, fused=True)
+    assert np.array_equal(lens2, lens)
+    assert torch.equal(as_bits(step2.scores), as_bits(step.scores)), f"draw {i}: scores differ"
+    assert torch.equal(step2.keep, step.keep), f"draw {i}: keep differs"
+    assert torch.equal(as_bits(case2.k), as_bits(case.k)) and torch.equal(as_bits(case2.v), as_bits(case.v)), \
+        f"draw {i}: caches differ"
+    log(f"draw {i}: {len(units)} sampled units match the oracle; rkv_step gives the same bytes")
