@@ -2,7 +2,9 @@
 and block size, head_dim, GQA group, window, budget and buffer, lambda,
 head-shared selection, ragged lengths on both sides of the trigger -- each
 run through the three calls and checked against the oracle on sampled units,
-and through rkv_step, which must give the same bytes."""
+and through rkv_step and rkv_step_device (lengths on the GPU), which must
+give the same bytes; bf16 draws also run the Gram redundancy against the
+oracle."""
 import math
 
 import numpy as np
@@ -10,7 +12,9 @@ import pytest
 import torch
 
 import rkv_synth as syn
-from gpu_harness import check_layer_shared, check_unit, log, make_case, run_step, sample_units
+from gpu_harness import (check_layer_shared, check_unit, config_of, log, make_case, run_step,
+                         sample_units)
+from kv_cache_compression_decode_amd.step import RKVStep
 
 pytestmark = pytest.mark.gpu
 
@@ -72,4 +76,29 @@ def test_random_configuration(i):
     assert torch.equal(step2.keep, step.keep), f"draw {i}: keep differs"
     assert torch.equal(as_bits(case2.k), as_bits(case.k)) and torch.equal(as_bits(case2.v), as_bits(case.v)), \
         f"draw {i}: caches differ"
-    log(f"draw {i}: {len(units)} sampled units match the oracle; rkv_step gives the same bytes")
+    # rkv_step_device on another fresh copy: the trigger taken on the GPU
+    case3 = make_case(spec)
+    maxn = int(max(spec.lens))
+    worst = 0
+    if spec.layout == "paged":
+        bs = spec.block_size
+        worst = spec.num_seqs * max(0, -(-maxn // bs) - -(-spec.budget // bs))
+    st3 = RKVStep(config_of(spec, shared), spec.num_seqs, maxn, free_capacity=worst)
+    st3.scores.fill_(float("nan"))
+    st3.keep.fill_(-7)
+    d_lens = torch.from_numpy(np.array(spec.lens, dtype=np.int32)).cuda()
+    st3.device(case3.cache, case3.q, d_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_lens.cpu().numpy(), lens), f"draw {i}: device lengths"
+    assert torch.equal(as_bits(st3.scores), as_bits(step.scores)), f"draw {i}: device scores differ"
+    assert torch.equal(st3.keep, step.keep), f"draw {i}: device keep differs"
+    assert torch.equal(as_bits(case3.k), as_bits(case.k)) and torch.equal(as_bits(case3.v), as_bits(case.v)), \
+        f"draw {i}: device caches differ"
+    if spec.dtype == "bf16":   # the Gram path on the untouched inputs
+        from test_gpu_gram import check_gram_unit, run_gram
+        case4 = make_case(spec)
+        red = run_gram(case4)
+        for u in units:
+            check_gram_unit(case4, red, *u)
+    log(f"draw {i}: {len(units)} sampled units match the oracle; rkv_step and rkv_step_device "
+        "give the same bytes")
