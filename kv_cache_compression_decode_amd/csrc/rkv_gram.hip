@@ -17,14 +17,16 @@
 // the four row tiles' chains of one block run interleaved, and a block's
 // entries are scaled by their column's r_i (while the next block's chains
 // run) and summed into per-row accumulators, so the matrix never leaves
-// registers.  The column factors
-// r_i are computed while a tile is staged (the four threads loading a key
-// reduce its squares across their lanes), so no pass over the keys precedes
-// the products and no workspace is needed.
+// registers (the build puts this file's MFMA results in VGPRs, where the
+// scaling reads them).  The column factors r_i are computed while a tile is
+// staged (the four threads loading a key reduce its squares across their
+// lanes), so no pass over the keys precedes the products and no workspace is
+// needed.
 //
 // Workgroups are mapped so that the row blocks of a unit run on one XCD
-// (workgroup b runs on XCD b % 8): the unit's keys are read from HBM into
-// that XCD's L2 once and re-read from there by its other row blocks.
+// (workgroup b runs on XCD b % 8), so a unit's later row blocks can find its
+// keys in that XCD's L2; with more units in flight than an L2 holds, part of
+// them come from HBM again (about 1.5 reads of every key at 1152 keys).
 //
 // The rank-one form in the scoring kernels gives the same values up to
 // rounding with O(N d) work instead of O(N^2 d); this path computes the Gram
