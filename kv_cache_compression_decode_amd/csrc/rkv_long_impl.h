@@ -12,8 +12,10 @@
 //
 // Units are launched P at a time (P * C workgroups: as many as are resident
 // on the device at once), unit unit0 + i taken by workgroups C*i .. C*i+C-1,
-// so the C workgroups a span waits for are all running (work of other
-// streams can only delay some of them, never block them).  The wait is a
+// so the C workgroups a span waits for are all running.  Work of other kinds
+// on other streams can only delay some of them (it finishes and frees its
+// room); two such span launches at once on one device could hold each
+// other's room, which is why the interface asks for them on one stream.  The wait is a
 // spin on a per-unit counter (zeroed by a small kernel first), bounded at
 // one second so that no launch can hang the device; a launch that reached
 // the bound would finish with wrong scores -- it is never reached when the
