@@ -58,7 +58,12 @@ def parse():
                    help="time rkv_window_store (one decode step's queries, all layers, into the ring)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed region, one 256 MiB device copy (counter calibration)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.steps is not None and args.steps < 1:
+        p.error("--steps must be >= 1")
+    if args.warmup < 0:
+        p.error("--warmup must be >= 0")
+    return args
 
 
 def fused_launch(spec, trig_lens) -> bool:

@@ -77,3 +77,10 @@ def test_committed_counter_summaries_name_a_kernel_and_workload():
         assert kernel in b.KERNEL_SOURCES, f
         text = open(os.path.join(prof, f)).read()
         assert "source_hash:" in text and "hbm_bytes_per_launch:" in text and "rocprofv3" in text, f
+
+
+@pytest.mark.parametrize("argv", [["--steps", "0"], ["--warmup", "-1"]])
+def test_bad_step_counts_are_rejected(argv):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "must be" in r.stderr
