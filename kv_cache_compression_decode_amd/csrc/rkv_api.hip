@@ -366,7 +366,9 @@ rkv_status rkv_redundancy_gram(const rkv_config* cfg, const rkv_cache* cache, in
     fill_table(a.tt, trig, first, cnt, nullptr);
     a.g.num_trig = cnt;
     a.units = cnt * cfg->num_layers * cfg->num_kv_heads;
-    a.rblocks = rkv::gram_row_blocks(max_len_of(trig, first, cnt));
+    const int longest = max_len_of(trig, first, cnt);
+    a.rows = rkv::gram_block_rows(longest, cfg->head_dim);
+    a.rblocks = (longest + a.rows - 1) / a.rows;
     const hipError_t e = rkv::launch_gram(a, hs);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
   }

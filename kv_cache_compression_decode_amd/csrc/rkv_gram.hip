@@ -9,12 +9,12 @@
 // (exact operands; no rounding of normalised keys) and the two scalings are
 // applied in fp32:  R_j = (r_j * sum_i (k_j . k_i) r_i - r_j^2 |k_j|^2) / (N-1).
 //
-// A workgroup takes 256 rows of a unit (4 waves x 64 rows, held as MFMA A
-// operands in registers; a wave whose rows all lie past N skips the
+// A workgroup takes 256 or 384 rows of a unit (4 waves x 64 or 96 rows, held
+// as MFMA A operands in registers; a wave whose rows all lie past N skips the
 // products) and streams all of the unit's keys through LDS in
 // double-buffered 64-key tiles.  Each 16 x 16 block of k_j . k_i is one chain
 // of v_mfma_f32_16x16x32_bf16 (fp32 accumulation) over the head dimension;
-// the four row tiles' chains of one block run interleaved, and a block's
+// the row tiles' chains of one block run interleaved, and a block's
 // entries are scaled by their column's r_i (while the next block's chains
 // run) and summed into per-row accumulators, so the matrix never leaves
 // registers (the build puts this file's MFMA results in VGPRs, where the
@@ -38,10 +38,8 @@ namespace rkv {
 
 namespace {
 
-constexpr int kWaveRows = 64;                          // rows per wave: 4 MFMA row tiles
-constexpr int kRowTiles = kWaveRows / 16;
-constexpr int kGramRows = kWaveRows * kThreads / kWave;  // rows per workgroup
 constexpr int kGramTile = 64;    // keys per LDS tile
+constexpr int kWavesPerGroup = kThreads / kWave;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes, a native vector
 
 // Sum of squares of the 8 bf16 values of a 16-byte piece (fp32, exact products).
@@ -89,8 +87,14 @@ __device__ __forceinline__ void gram_stage(const u32x4 (&pre)[D / 32], uint16_t*
   if (sq == 0) tinv[sk] = ss > 0.f ? fast_rsqrt(ss) : 0.f;
 }
 
-template <bool PAGED, int D>
+// WR rows per wave (WR / 16 MFMA row tiles): each column fragment read from
+// LDS feeds WR / 16 products, so more rows per wave mean less LDS traffic per
+// product but more registers (at head_dim 128: 156 VGPRs and 3 waves per SIMD
+// at 64 rows, 231 and 2 at 96).
+template <bool PAGED, int D, int WR>
 __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
+  constexpr int kWaveRows = WR, kRowTiles = WR / 16, kGramRows = WR * kWavesPerGroup;
+  static_assert(WR % 16 == 0, "whole row tiles");
   constexpr int KS = D / 32;                             // MFMA k-steps over the head dimension
   constexpr int P = D + 8;                               // LDS row pitch (elements)
   constexpr int QD = D / 4;                              // staging: 4 threads per key, QD dims each
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   static_assert(kGramTile * 4 == kThreads, "one key per 4 threads when staging");
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGramTile * P];
   __shared__ float tinv[2][kGramTile];                  // r_i of the tile's keys
-  __shared__ float nrm2[kThreads / kWave][kWaveRows];   // |k_j|^2 of each wave's rows
+  __shared__ float nrm2[kWavesPerGroup][kWaveRows];     // |k_j|^2 of each wave's rows
 
   // work item of this workgroup: consecutive items (one unit's row blocks) on one XCD
   const int total = a.units * a.rblocks;
@@ -210,22 +214,34 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
     }
 }
 
-template <bool PAGED, int D>
+template <bool PAGED, int D, int WR>
 hipError_t launch_gram_t(const GramArgs& a, hipStream_t st) {
   const int total = a.units * a.rblocks;
   const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((gram_rowsum_kernel<PAGED, D>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((gram_rowsum_kernel<PAGED, D, WR>), dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gram_row_blocks(int max_len) { return (max_len + kGramRows - 1) / kGramRows; }
+// Rows per workgroup for a launch whose longest unit has max_len keys.  At
+// head_dim 128 the 384-row form is taken when its last row block wastes fewer
+// rows than the 256-row form's (1152 keys: 3 full blocks against 4.5); with
+// equal waste, and at head_dim 64, 256 rows.
+int gram_block_rows(int max_len, int d) {
+  constexpr int kSmall = 64 * kWavesPerGroup, kLarge = 96 * kWavesPerGroup;
+  if (d != 128) return kSmall;
+  const long waste_small = (long)(max_len + kSmall - 1) / kSmall * kSmall - max_len;
+  const long waste_large = (long)(max_len + kLarge - 1) / kLarge * kLarge - max_len;
+  return waste_large < waste_small ? kLarge : kSmall;
+}
 
 hipError_t launch_gram(const GramArgs& a, hipStream_t st) {
   if (a.units == 0 || a.rblocks == 0) return hipSuccess;
-  if (a.g.d == 64) return a.g.paged ? launch_gram_t<true, 64>(a, st) : launch_gram_t<false, 64>(a, st);
-  return a.g.paged ? launch_gram_t<true, 128>(a, st) : launch_gram_t<false, 128>(a, st);
+  if (a.g.d == 64) return a.g.paged ? launch_gram_t<true, 64, 64>(a, st) : launch_gram_t<false, 64, 64>(a, st);
+  if (a.rows == 96 * kWavesPerGroup)
+    return a.g.paged ? launch_gram_t<true, 128, 96>(a, st) : launch_gram_t<false, 128, 96>(a, st);
+  return a.g.paged ? launch_gram_t<true, 128, 64>(a, st) : launch_gram_t<false, 128, 64>(a, st);
 }
 
 }  // namespace rkv

@@ -76,7 +76,8 @@ struct GramArgs {
   float* red;             // [L][S][Hkv][stride]
   int32_t stride;
   int32_t units;          // triggered units of this launch (num_trig * L * Hkv)
-  int32_t rblocks;        // 128-row blocks per unit: gram_row_blocks(longest length)
+  int32_t rows;           // rows per workgroup: gram_block_rows(longest length, d)
+  int32_t rblocks;        // row blocks per unit: longest length / rows, rounded up
 };
 
 // Window-query ring store (rkv_window_store).
@@ -90,7 +91,7 @@ struct WindowArgs {
 
 hipError_t launch_window_store(const WindowArgs& a, hipStream_t st);
 hipError_t launch_table(const TableArgs& a, hipStream_t st);
-int gram_row_blocks(int max_len);
+int gram_block_rows(int max_len, int d);
 hipError_t launch_gram(const GramArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, bool bf16, hipStream_t st);
 // true if launch_step can run this launch's units (else use the three kernels)

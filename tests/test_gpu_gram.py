@@ -6,7 +6,9 @@ The products take the cached bf16 keys exactly and sum in float32, so the
 bar is tighter than the scoring kernels': |R_gpu - R| <= 1e-4 * max|R| + 1e-6
 per unit.  Also: agreement with rkv_score's redundancy output (the rank-one
 form) within the scoring tolerance, untouched rows and columns, zero keys,
-and ragged, paged, head_dim 64 and maximum-length units."""
+and ragged, paged, head_dim 64 and maximum-length units, in both workgroup
+forms (256 and 384 rows; a launch takes the one whose last row block wastes
+fewer rows)."""
 import numpy as np
 import pytest
 import torch
@@ -91,6 +93,15 @@ CASES = {
                                             num_blocks=8, lens=(1600, 2100)),
     "runs-dups": syn.config(4).with_(name="g-runs", seed=47, num_seqs=2, num_layers=1,
                                      lens=(1152, 1152)),
+    # longest unit 1100 keys at head_dim 128: the 384-row workgroups (their last
+    # block wastes 52 rows against the 256-row form's 180); units ending 2 and 1
+    # rows into a block, one unit shorter than a block, one below the trigger
+    "rows384-ragged": syn.config(1).with_(name="g-384", seed=51, num_seqs=4, num_layers=2,
+                                           num_q_heads=8, num_kv_heads=2, budget=256, buffer=32,
+                                           lens=(1100, 770, 385, 250)),
+    "rows384-paged-bs16": syn.config(3).with_(name="g-384p", seed=52, num_seqs=3, num_layers=2,
+                                               num_q_heads=8, num_kv_heads=2, budget=300,
+                                               buffer=45, num_blocks=220, lens=(1100, 800, 350)),
 }
 
 
