@@ -12,7 +12,7 @@
 // A workgroup takes 256 or 384 rows of a unit (4 waves x 64 or 96 rows, held
 // as MFMA A operands in registers; a wave whose rows all lie past N skips the
 // products) and streams all of the unit's keys through LDS in
-// double-buffered 64-key tiles.  Each 16 x 16 block of k_j . k_i is one chain
+// double-buffered tiles of 64 keys (128 for the 384-row form).  Each 16 x 16 block of k_j . k_i is one chain
 // of v_mfma_f32_16x16x32_bf16 (fp32 accumulation) over the head dimension;
 // the row tiles' chains of one block run interleaved, and a block's
 // entries are scaled by their column's r_i (while the next block's chains
@@ -38,8 +38,12 @@ namespace rkv {
 
 namespace {
 
-constexpr int kGramTile = 64;    // keys per LDS tile
+constexpr int kStageKeys = kThreads / 4;   // keys staged per pass: 4 threads per key
 constexpr int kWavesPerGroup = kThreads / kWave;
+// Keys per LDS tile: 64, or 128 for the 96-row form at head_dim 128 (half the
+// barriers per workgroup; 72 KB of LDS, two workgroups per CU as its
+// registers allow anyway).
+constexpr int kTile64 = 64, kTile96 = 128;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes, a native vector
 
 // Sum of squares of the 8 bf16 values of a 16-byte piece (fp32, exact products).
@@ -59,48 +63,57 @@ __device__ __forceinline__ float sum_quad(float v) {
   return v;
 }
 
-// Staging of a 64-key tile: thread (sk, sq) loads dims [QD sq, QD sq + QD) of
-// key sk of tile kt (keys at or past n are zeros) ...
-template <bool PAGED, int D>
-__device__ __forceinline__ void gram_load(u32x4 (&pre)[D / 32], const uint16_t* kc, const KeyRows<PAGED>& rows,
-                                          int kt, int n, int sk, int sq) {
+// Staging of a tile of 64 KPT keys: thread (sk, sq) loads dims
+// [QD sq, QD sq + QD) of keys sk, sk + 64, .. of tile kt (keys at or past n
+// are zeros) ...
+template <bool PAGED, int D, int KPT>
+__device__ __forceinline__ void gram_load(u32x4 (&pre)[KPT][D / 32], const uint16_t* kc,
+                                          const KeyRows<PAGED>& rows, int kt, int n, int sk, int sq) {
   constexpr int QD = D / 4, PPT = D / 32;
-  const int key = kt * kGramTile + sk;
-  const u32x4* src = reinterpret_cast<const u32x4*>(kc + rows.at(key < n ? key : 0) + QD * sq);
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) pre[i] = key < n ? src[i] : u32x4{0u, 0u, 0u, 0u};
+  for (int kk = 0; kk < KPT; ++kk) {
+    const int key = (kt * KPT + kk) * kStageKeys + sk;
+    const u32x4* src = reinterpret_cast<const u32x4*>(kc + rows.at(key < n ? key : 0) + QD * sq);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) pre[kk][i] = key < n ? src[i] : u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // ... then writes them to the LDS tile (row pitch D + 8) and, with the other
-// three threads of its key, the key's 1/|k| (0 for a zero key).
-template <int D>
-__device__ __forceinline__ void gram_stage(const u32x4 (&pre)[D / 32], uint16_t* tile, float* tinv, int sk,
+// three threads of each key, the key's 1/|k| (0 for a zero key).
+template <int D, int KPT>
+__device__ __forceinline__ void gram_stage(const u32x4 (&pre)[KPT][D / 32], uint16_t* tile, float* tinv, int sk,
                                            int sq) {
   constexpr int QD = D / 4, PPT = D / 32, P = D + 8;
-  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    *reinterpret_cast<u32x4*>(&tile[sk * P + QD * sq + 8 * i]) = pre[i];
-    ss = sq8(pre[i], ss);
+  for (int kk = 0; kk < KPT; ++kk) {
+    const int r = kk * kStageKeys + sk;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      *reinterpret_cast<u32x4*>(&tile[r * P + QD * sq + 8 * i]) = pre[kk][i];
+      ss = sq8(pre[kk][i], ss);
+    }
+    ss = sum_quad(ss);
+    if (sq == 0) tinv[r] = ss > 0.f ? fast_rsqrt(ss) : 0.f;
   }
-  ss = sum_quad(ss);
-  if (sq == 0) tinv[sk] = ss > 0.f ? fast_rsqrt(ss) : 0.f;
 }
 
 // WR rows per wave (WR / 16 MFMA row tiles): each column fragment read from
 // LDS feeds WR / 16 products, so more rows per wave mean less LDS traffic per
 // product but more registers (at head_dim 128: 156 VGPRs and 3 waves per SIMD
-// at 64 rows, 231 and 2 at 96).
-template <bool PAGED, int D, int WR>
+// at 64 rows, 231 and 2 at 96).  TILE keys per LDS tile (a multiple of 64).
+template <bool PAGED, int D, int WR, int TILE>
 __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   constexpr int kWaveRows = WR, kRowTiles = WR / 16, kGramRows = WR * kWavesPerGroup;
+  constexpr int kGramTile = TILE, KPT = TILE / kStageKeys;
   static_assert(WR % 16 == 0, "whole row tiles");
+  static_assert(TILE % kStageKeys == 0, "whole staging passes per tile");
   constexpr int KS = D / 32;                             // MFMA k-steps over the head dimension
   constexpr int P = D + 8;                               // LDS row pitch (elements)
   constexpr int QD = D / 4;                              // staging: 4 threads per key, QD dims each
   constexpr int PPT = QD / 8;                            // 16-byte pieces per thread per tile
   constexpr int CT = kGramTile / 16;                     // 16-key column blocks per tile
-  static_assert(kGramTile * 4 == kThreads, "one key per 4 threads when staging");
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGramTile * P];
   __shared__ float tinv[2][kGramTile];                  // r_i of the tile's keys
   __shared__ float nrm2[kWavesPerGroup][kWaveRows];     // |k_j|^2 of each wave's rows
@@ -138,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   // staging: four threads per key
   const int sk = t >> 2, sq = t & 3;
   const int ntiles = (n + kGramTile - 1) / kGramTile;
-  u32x4 pre[PPT];
-  gram_load<PAGED, D>(pre, kc, rows, 0, n, sk, sq);
-  gram_stage<D>(pre, &tile[0][0], tinv[0], sk, sq);
+  u32x4 pre[KPT][PPT];
+  gram_load<PAGED, D, KPT>(pre, kc, rows, 0, n, sk, sq);
+  gram_stage<D, KPT>(pre, &tile[0][0], tinv[0], sk, sq);
   lds_barrier();
 
   float racc[kRowTiles][4];
@@ -151,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < ntiles;
-    if (more) gram_load<PAGED, D>(pre, kc, rows, kt + 1, n, sk, sq);   // in flight during the products
+    if (more) gram_load<PAGED, D, KPT>(pre, kc, rows, kt + 1, n, sk, sq);   // in flight during the products
     if (live) {
       // Block ct's four row-tile chains go into c[ct & 1] while block ct - 1's
       // results are scaled by their columns' r_i and summed into the rows.
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
         }
       }
     }
-    if (more) gram_stage<D>(pre, &tile[cur ^ 1][0], tinv[cur ^ 1], sk, sq);
+    if (more) gram_stage<D, KPT>(pre, &tile[cur ^ 1][0], tinv[cur ^ 1], sk, sq);
     lds_barrier();
   }
 
@@ -214,11 +227,11 @@ __global__ __launch_bounds__(kThreads) void gram_rowsum_kernel(GramArgs a) {
     }
 }
 
-template <bool PAGED, int D, int WR>
+template <bool PAGED, int D, int WR, int TILE>
 hipError_t launch_gram_t(const GramArgs& a, hipStream_t st) {
   const int total = a.units * a.rblocks;
   const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((gram_rowsum_kernel<PAGED, D, WR>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((gram_rowsum_kernel<PAGED, D, WR, TILE>), dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -238,10 +251,10 @@ int gram_block_rows(int max_len, int d) {
 
 hipError_t launch_gram(const GramArgs& a, hipStream_t st) {
   if (a.units == 0 || a.rblocks == 0) return hipSuccess;
-  if (a.g.d == 64) return a.g.paged ? launch_gram_t<true, 64, 64>(a, st) : launch_gram_t<false, 64, 64>(a, st);
+  if (a.g.d == 64) return a.g.paged ? launch_gram_t<true, 64, 64, kTile64>(a, st) : launch_gram_t<false, 64, 64, kTile64>(a, st);
   if (a.rows == 96 * kWavesPerGroup)
-    return a.g.paged ? launch_gram_t<true, 128, 96>(a, st) : launch_gram_t<false, 128, 96>(a, st);
-  return a.g.paged ? launch_gram_t<true, 128, 64>(a, st) : launch_gram_t<false, 128, 64>(a, st);
+    return a.g.paged ? launch_gram_t<true, 128, 96, kTile96>(a, st) : launch_gram_t<false, 128, 96, kTile96>(a, st);
+  return a.g.paged ? launch_gram_t<true, 128, 64, kTile64>(a, st) : launch_gram_t<false, 128, 64, kTile64>(a, st);
 }
 
 }  // namespace rkv
