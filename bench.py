@@ -380,6 +380,8 @@ def main():
                    "mix_lambda": spec.mix_lambda, "layout": spec.layout,
                    "triggered_units": units},
         "tokens_scored_per_s": round(tokens / (ms * 1e-3), 1),
+        # sequence tokens whose caches were compressed (sum of the triggered lengths) per second
+        "cache_tokens_per_s": round(int(sum(int(n) for n in lens0[trig])) / (ms * 1e-3), 1),
         "entry": "rkv_score+rkv_select+rkv_compact" if args.three_calls else "rkv_step",
         "selection": "head-shared" if args.shared else "per kv head",
         "roofline": roofline,

@@ -29,6 +29,9 @@ def test_bench_prints_one_contract_line():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["unit"] == "steps/s" and d["value"] > 0 and d["higher_is_better"] is True
     assert d["config"]["workload"] == "llama8b-1seq"
+    # rates: one 1152-token sequence per step, scored on 32 layers x 8 kv heads
+    assert abs(d["cache_tokens_per_s"] - d["value"] * 1152) <= 1e-3 * d["cache_tokens_per_s"]
+    assert abs(d["tokens_scored_per_s"] - d["cache_tokens_per_s"] * 32 * 8) <= 1e-3 * d["tokens_scored_per_s"]
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
