@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload index (0-4)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the CPU-baseline sample (0 skips it)")
+    p.add_argument("--device-lens", action="store_true",
+                   help="time rkv_step_device (lengths in device memory, the trigger table built "
+                        "by a kernel: the form a captured decode graph uses) instead of rkv_step")
     p.add_argument("--three-calls", action="store_true",
                    help="time rkv_score + rkv_select + rkv_compact instead of rkv_step")
     p.add_argument("--shared", action="store_true",
@@ -246,6 +249,11 @@ def main():
         else:
             caches.append(B.make_cache(kc, vc, capacity=case.cap))
     lens_per = [lens0.copy() for _ in range(nsteps)]
+    if args.device_lens:
+        if restore or args.three_calls:
+            raise SystemExit("--device-lens times rkv_step_device alone, on workloads whose caches "
+                             "are copied per step")
+        d_lens_per = [torch.from_numpy(lens0.copy()).to(dev) for _ in range(nsteps)]
     # --three-calls: events around each of the three kernels (a breakdown;
     # the markers themselves add GPU time between launches).  rkv_step: one
     # event pair around the whole timed region, so nothing runs between the
@@ -277,9 +285,15 @@ def main():
             e[2].record(stream)
             step.compact(caches[i], lens_per[i], stream)
             e[3].record(stream)
+        elif args.device_lens:
+            step.device(caches[i], case.q, d_lens_per[i], stream)
         else:
             step.fused(caches[i], case.q, lens_per[i], stream)
 
+    if args.device_lens:   # workspace and free counts allocated outside the timed region
+        step.device(caches[0], case.q, torch.from_numpy(lens0.copy()).to(dev), stream)
+        copies[0][0].copy_(case.k)   # copy 0 back to its pristine contents
+        copies[0][1].copy_(case.v)
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
@@ -301,6 +315,11 @@ def main():
     keep = step.keep.view(spec.num_layers, spec.num_seqs, spec.num_kv_heads, spec.budget)
     keep = keep.cpu().numpy()[:, trig].reshape(-1, spec.budget)
     moved_rows = int((keep != np.arange(spec.budget)[None, :]).sum()) if units else 0
+    if args.device_lens:   # every step left the compacted lengths in its device tensor
+        want = np.where(trig, spec.budget, lens0).astype(np.int32)
+        for i, d in enumerate(d_lens_per):
+            if not np.array_equal(d.cpu().numpy(), want):
+                raise RuntimeError(f"rkv_step_device step {i}: device lengths {d.cpu().numpy()} != {want}")
 
     ms = (t1 - t0) * 1e3 / args.steps
     region_us = region[0].elapsed_time(region[1]) * 1e3 / args.steps
@@ -382,11 +401,14 @@ def main():
         "tokens_scored_per_s": round(tokens / (ms * 1e-3), 1),
         # sequence tokens whose caches were compressed (sum of the triggered lengths) per second
         "cache_tokens_per_s": round(int(sum(int(n) for n in lens0[trig])) / (ms * 1e-3), 1),
-        "entry": "rkv_score+rkv_select+rkv_compact" if args.three_calls else "rkv_step",
+        "entry": ("rkv_score+rkv_select+rkv_compact" if args.three_calls else
+                  "rkv_step_device" if args.device_lens else "rkv_step"),
         "selection": "head-shared" if args.shared else "per kv head",
         "roofline": roofline,
         "kernels": kern,
         "kernel_timing": ("HIP events around each kernel" if args.three_calls else
+                          "HIP events around the timed region / steps (the table kernel and the step "
+                          "kernel per step)" if args.device_lens else
                           "HIP events around the timed region / steps (one kernel per step)")
                          + ("; cache blocks restored between steps outside the timed intervals, "
                             "ms_per_step = mean per-step event interval" if restore else ""),

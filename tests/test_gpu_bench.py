@@ -38,3 +38,15 @@ def test_bench_prints_one_contract_line():
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+def test_bench_device_lens_line():
+    """--device-lens times rkv_step_device (trigger table built on the GPU);
+    bench.py itself checks every step's device lengths afterwards."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--cpu-seconds", "0", "--device-lens"], capture_output=True, text=True,
+                       timeout=280, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    assert d["entry"] == "rkv_step_device" and d["value"] > 0 and d["steps"] == 3
+    assert d["roofline"]["bound"] == "hbm" and d["roofline"]["achieved"] > 0
