@@ -27,14 +27,14 @@ Numbers: bf16 inputs are widened exactly to float64; all arithmetic is float64.
 from __future__ import annotations
 
 import math
-from typing import Dict, List, Sequence
+from typing import List, Sequence
 
 import numpy as np
 
 __all__ = [
     "decode", "is_triggered", "window_logits", "importance", "cosine_gram",
     "redundancy", "mixed_score", "score_unit", "select_keep", "compact_rows",
-    "free_blocks", "unit_step", "q_group", "step_contiguous", "step_unit",
+    "free_blocks", "unit_step", "q_group", "step_unit",
     "shared_score", "select_keep_shared", "layer_step_shared", "redundancy_at",
     "window_store",
 ]
@@ -224,38 +224,6 @@ def q_group(q_seq_layer: np.ndarray, h: int, group: int) -> np.ndarray:
     head j uses kv head j // group): (group, w, d) -> (group*w, d)."""
     qg = q_seq_layer[h * group:(h + 1) * group]
     return qg.reshape(-1, qg.shape[-1])
-
-
-def step_contiguous(spec, k, v, q, lens, shared: bool = False) -> Dict[str, object]:
-    """Whole step over contiguous caches k, v (L, S, Hkv, cap, d) and window
-    queries q (L, S, Hq, w, d), all in storage dtype.  Returns per-unit results
-    of triggered sequences and the new lengths.  shared: the head-shared
-    selection of layer_step_shared.  Meant for small cases."""
-    group = spec.num_q_heads // spec.num_kv_heads
-    out = {"units": {}, "lens": np.array(lens, dtype=np.int64).copy()}
-    for s in range(spec.num_seqs):
-        n = int(lens[s])
-        if not is_triggered(n, spec.budget, spec.buffer):
-            continue
-        for l in range(spec.num_layers):
-            qd = decode(q[l, s], spec.dtype)
-            heads = range(spec.num_kv_heads)
-            if shared:
-                res = layer_step_shared(
-                    [q_group(qd, h, group) for h in heads],
-                    [decode(k[l, s, h, :n], spec.dtype) for h in heads],
-                    [k[l, s, h, :n] for h in heads], [v[l, s, h, :n] for h in heads],
-                    spec.budget, spec.window, spec.mix_lambda)
-                for h in heads:
-                    out["units"][(s, l, h)] = res[h]
-                continue
-            for h in heads:
-                out["units"][(s, l, h)] = unit_step(
-                    q_group(qd, h, group), decode(k[l, s, h, :n], spec.dtype),
-                    k[l, s, h, :n], v[l, s, h, :n], spec.budget, spec.window,
-                    spec.mix_lambda)
-        out["lens"][s] = spec.budget
-    return out
 
 
 def step_unit(spec, q_sl, k_rows, v_rows, h):

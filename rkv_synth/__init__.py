@@ -39,7 +39,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Spec", "CONFIGS", "config", "seq_lens", "triggered_mask_by_length",
+    "Spec", "CONFIGS", "config", "seq_lens",
     "dup_plan", "key_means", "keys", "values", "queries", "block_table",
     "to_bf16_bits", "storage_dtype", "build_contiguous", "build_paged",
     "build_queries", "CANARY_BF16", "CANARY_F32",
@@ -155,13 +155,6 @@ def seq_lens(spec: Spec) -> np.ndarray:
     lo, hi = spec.len_range
     rng = np.random.default_rng([spec.seed, 0])
     return rng.integers(lo, hi + 1, size=spec.num_seqs).astype(np.int32)
-
-
-def triggered_mask_by_length(spec: Spec, lens: Optional[np.ndarray] = None) -> np.ndarray:
-    """Which sequences are at or past budget + buffer (a length comparison;
-    the oracle owns the rule it implements, this only sizes test inputs)."""
-    lens = seq_lens(spec) if lens is None else lens
-    return lens >= spec.budget + spec.buffer
 
 
 # ---------------------------------------------------------------- duplicates

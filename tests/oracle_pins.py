@@ -12,6 +12,7 @@ from __future__ import annotations
 import json
 import math
 import os
+import struct
 
 import numpy as np
 
@@ -84,6 +85,93 @@ def pin_golden_free_blocks(o):
 def pin_golden_trigger(o):
     for ex in golden("hand_examples.json")["trigger"]:
         assert bool(o.is_triggered(ex["n"], ex["budget"], ex["buffer"])) == ex["expect"], ex
+
+
+# ------------------------------------------------------------- storage decode
+
+def _bf16_by_struct(bits):
+    """bf16 bits -> float through the standard library: the 16 bits are the
+    top half of an IEEE-754 binary32 (sign, 8-bit exponent, 7 mantissa bits)."""
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def pin_decode_bf16_known_patterns(o):
+    """Fixed bf16 patterns with values known from the binary32 format."""
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x8000: -0.0, 0x0000: 0.0,
+             0x4049: 3.140625, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x0080: 2.0 ** -126,
+             0xBF40: -0.75, 0x3C00: 2.0 ** -7, 0x7F80: math.inf, 0xFF80: -math.inf}
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = o.decode(bits, "bf16")
+    assert got.dtype == np.float64
+    for b, g in zip(cases, got):
+        want = cases[b]
+        assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want), (hex(b), g, want)
+    with np.errstate(invalid="ignore"):
+        assert np.isnan(o.decode(np.array([0x7FC0, 0xFFC1], dtype=np.uint16), "bf16")).all()
+
+
+def pin_decode_bf16_random_patterns(o):
+    """Every finite random bf16 pattern decodes to torch's bfloat16 -> float64
+    widening and to the struct-level reading of the format; shapes are kept."""
+    import torch
+    rng = np.random.default_rng([77, 4])
+    bits = rng.integers(0, 1 << 16, size=(64, 33), dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    got = o.decode(bits, "bf16")
+    assert got.shape == bits.shape
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got[finite], ref[finite])
+    for b in bits.ravel()[:300]:
+        if (int(b) & 0x7F80) != 0x7F80:
+            assert o.decode(np.array([b], dtype=np.uint16), "bf16")[0] == _bf16_by_struct(b)
+
+
+def pin_decode_f32(o):
+    """float32 storage widens exactly: values from their binary32 bit patterns
+    (read by struct), subnormals and signed zero included."""
+    rng = np.random.default_rng([77, 5])
+    pats = [0x3F800000, 0xC0000000, 0x00000001, 0x80000000, 0x007FFFFF, 0x7F7FFFFF, 0x3EAAAAAB]
+    pats += [int(x) for x in rng.integers(0, 0x7F000000, size=100)]
+    vals = [struct.unpack("<f", struct.pack("<I", p))[0] for p in pats]
+    arr = np.array(pats, dtype=np.uint32).view(np.float32)
+    got = o.decode(arr, "f32")
+    assert got.dtype == np.float64
+    for g, want in zip(got, vals):
+        assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want)
+
+
+def pin_step_unit_gqa(o):
+    """step_unit, the per-unit entry the GPU comparisons use: with G = 3 query
+    heads per KV head, each KV head h (h = 0, 1, 2) is scored from query heads
+    3h .. 3h+2 only.  The expected values come from the scalar brute force on
+    rows sliced and decoded here by the standard library, and compaction
+    returns the stored bits of the kept rows."""
+    import torch
+    from types import SimpleNamespace
+    rng = np.random.default_rng([77, 6])
+    hkv, group, w, d, n = 3, 3, 2, 8, 24
+    spec = SimpleNamespace(num_q_heads=hkv * group, num_kv_heads=hkv, dtype="bf16",
+                           budget=16, window=w, mix_lambda=0.3)
+
+    def bf16_bits(x):
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    q_sl = bf16_bits(rng.standard_normal((hkv * group, w, d)))
+    for h in range(hkv):
+        k_rows = bf16_bits(rng.standard_normal((n, d)) + rng.standard_normal(d))
+        v_rows = bf16_bits(rng.standard_normal((n, d)))
+        q_rows = [[_bf16_by_struct(b) for b in q_sl[h * group + g, r]]
+                  for g in range(group) for r in range(w)]
+        keys = [[_bf16_by_struct(b) for b in row] for row in k_rows]
+        bi, br, bs, bkeep = brute.unit(q_rows, keys, spec.mix_lambda, spec.budget, w)
+        got = o.step_unit(spec, q_sl, k_rows, v_rows, h)
+        _close(got["imp"], bi)
+        _close(got["red"], br)
+        _close(got["score"], bs)
+        assert list(got["keep"]) == bkeep, h
+        assert got["k_new"].dtype == np.uint16 and np.array_equal(got["k_new"], k_rows[bkeep])
+        assert np.array_equal(got["v_new"], v_rows[bkeep])
 
 
 # ------------------------------------------------------------- invariants

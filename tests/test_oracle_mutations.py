@@ -56,6 +56,20 @@ MUTANTS = [
      "out[i, s, :, int(steps[s]) % window, :] = q_step[i, s]"),
     ("ring slot shifted by one", "out[layer0 + i, s, :, int(steps[s]) % window, :] = q_step[i, s]",
      "out[layer0 + i, s, :, (int(steps[s]) + 1) % window, :] = q_step[i, s]"),
+    ("bf16 decode without the 16-bit shift", "astype(np.uint32) << np.uint32(16)",
+     "astype(np.uint32) << np.uint32(8)"),
+    ("bf16 decode with swapped bytes", "w = np.asarray(x, dtype=np.uint16).astype",
+     "w = np.asarray(x, dtype=np.uint16).byteswap().astype"),
+    ("bf16 decode drops the sign", "w = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
+     "w = (np.asarray(x, dtype=np.uint16).astype(np.uint32) & np.uint32(0x7FFF)) << np.uint32(16)"),
+    ("f32 decode through half precision", "return np.asarray(x, dtype=np.float32).astype(np.float64)",
+     "return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)"),
+    ("step_unit with group 1", "return unit_step(q_group(qd, h, group),",
+     "return unit_step(q_group(qd, h, 1),"),
+    ("step_unit with the heads' order inverted", "return unit_step(q_group(qd, h, group),",
+     "return unit_step(q_group(qd, spec.num_kv_heads - 1 - h, group),"),
+    ("step_unit compacts the decoded keys", "decode(k_rows, spec.dtype), k_rows, v_rows,",
+     "decode(k_rows, spec.dtype), decode(k_rows, spec.dtype), v_rows,"),
     ("shared layer: per-head keep", "keep = select_keep_shared(np.stack([h[2] for h in heads]), n, budget, window)",
      "keep = select_keep(heads[0][2], n, budget, window)"),
 ]
