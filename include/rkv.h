@@ -33,12 +33,20 @@
  *     workgroups as the device holds at once, but two such launches running
  *     at the same time on different streams of one device can hold each
  *     other's room: run such calls on one stream (or one at a time).  The
- *     wait is bounded (one second), so the device never hangs; a wait that
- *     reaches the bound leaves that launch's scores wrong.
+ *     wait is bounded (one second by default, rkv_set_span_wait_us), so the
+ *     device never hangs.  A wait that reaches the bound sets
+ *     RKV_DEVICE_SPAN_TIMEOUT in the workspace's status word; selection and
+ *     compaction given that workspace then leave the keep rows and the cache
+ *     untouched, and rkv_device_status reports it.
  *   - Every argument is checked before anything is enqueued.  On an error the
  *     call returns a status other than RKV_OK, enqueues nothing and changes no
  *     output; rkv_last_error() then describes it.  No C++ exception crosses
  *     this interface.  A device fault of earlier work shows up as RKV_ERR_HIP.
+ *   - Checks that need device data (a key-span wait that timed out, a block
+ *     id outside the pool) are recorded in the status word at the start of
+ *     the workspace (see rkv_device_status): the calls given that workspace
+ *     then skip every later write of the step, so the cache keeps its input
+ *     contents.
  *   - Sequence lengths live on the host.  Sequences below the trigger are
  *     untouched: their cache rows, score rows and keep rows are not written.
  *   - A call covers all layers and all triggered sequences of the batch.
@@ -49,6 +57,10 @@
  *                     token t of sequence s lives in physical block
  *                     block_table[s * max_blocks_per_seq + t / block_size],
  *                     row t % block_size; every layer uses the same table.
+ *                     Block ids must lie in [0, num_blocks): they are checked
+ *                     only with cfg->check_block_table = 1 (below).
+ *   layer stride    : cache->layer_stride elements from layer l to layer l + 1
+ *                     of K (and of V); 0 means the packed layouts above.
  *   window queries  : [num_layers][num_seqs][num_q_heads][window][head_dim]
  *                     query head j belongs to kv head j / (num_q_heads / num_kv_heads)
  *   scores, I, R    : float32 [num_layers][num_seqs][num_kv_heads][score_stride]
@@ -69,11 +81,16 @@ typedef enum rkv_status {
   RKV_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent arguments   */
   RKV_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels handle  */
   RKV_ERR_WORKSPACE = 3,    /* workspace missing or too small                   */
-  RKV_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed       */
+  RKV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed       */
+  RKV_ERR_DEVICE_CHECK = 5  /* a check on the device failed (rkv_device_status) */
 } rkv_status;
 
 typedef enum rkv_dtype { RKV_DTYPE_F32 = 0, RKV_DTYPE_BF16 = 1 } rkv_dtype;
 typedef enum rkv_layout { RKV_LAYOUT_CONTIGUOUS = 0, RKV_LAYOUT_PAGED = 1 } rkv_layout;
+
+/* Status word flags (rkv_device_status). */
+#define RKV_DEVICE_SPAN_TIMEOUT 1u  /* a key-span wait reached its bound           */
+#define RKV_DEVICE_BAD_BLOCK_ID 2u  /* a block-table id outside [0, num_blocks)    */
 
 /* Longest cache (tokens per sequence) the kernels accept. */
 #define RKV_MAX_LEN 32768
@@ -104,12 +121,29 @@ typedef struct rkv_config {
                                describes for tensor-parallel ranks ("How R-KV
                                decides what to drop").  Scores are still per
                                head; every head's keep row holds the same list. */
+  int32_t check_block_table; /* paged, 0 or 1.  1: before any kernel reads the
+                               pool, every block id a triggered sequence uses
+                               (logical blocks [0, ceil(len / block_size))) is
+                               checked against [0, num_blocks); a bad id sets
+                               RKV_DEVICE_BAD_BLOCK_ID and no kernel of the
+                               call reads or writes the pool.  Needs a
+                               workspace in every call that reads the pool
+                               (rkv_redundancy_gram does not check). */
 } rkv_config;
 
 /* The KV cache the step reads and compacts (device memory, caller-owned). */
 typedef struct rkv_cache {
   void *k;                          /* keys   (layout above)                    */
   void *v;                          /* values (same layout as k)                */
+  int64_t layer_stride;             /* elements from one layer to the next, for
+                                       K and V alike; 0 = packed.  Otherwise at
+                                       least the packed layer size (S*Hkv*cap*d
+                                       or num_blocks*Hkv*block_size*d) and a
+                                       multiple of 16 bytes, so that layers
+                                       padded apart in one allocation are used
+                                       in place (the R-KV project page, "How
+                                       R-KV decides what to drop", scores all
+                                       layers in one batched pass).             */
   int32_t capacity;                 /* contiguous: token slots per (l, s, h)    */
   int32_t num_blocks;               /* paged: blocks per layer in the pool      */
   const int32_t *block_table;       /* paged: device int32 [num_seqs][max_blocks_per_seq] */
@@ -128,7 +162,9 @@ const char *rkv_last_error(void);
 int32_t rkv_is_triggered(const rkv_config *cfg, int32_t len);
 
 /* Bytes of device workspace rkv_score needs for any batch of at most
- * num_seqs sequences of at most max_len tokens.  0 on invalid arguments. */
+ * num_seqs sequences of at most max_len tokens.  0 on invalid arguments.
+ * The first 256 bytes hold the status word (rkv_device_status); the same
+ * workspace is then passed to rkv_select and rkv_compact. */
 size_t rkv_workspace_size(const rkv_config *cfg, int32_t num_seqs, int32_t max_len);
 
 /* Step 1, scoring: I, R and S of every cached token of every triggered unit,
@@ -140,7 +176,8 @@ size_t rkv_workspace_size(const rkv_config *cfg, int32_t num_seqs, int32_t max_l
  *              rows written; score_stride >= the longest triggered length
  *   importance, redundancy  device float32 like scores, or NULL to skip
  *   workspace  device, >= rkv_workspace_size(cfg, num_seqs, max len), 256-byte
- *              aligned; contents on entry are ignored
+ *              aligned; contents on entry are ignored.  The call clears its
+ *              status word, then records what its kernels find there.
  * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED (head_dim, window rows,
  * length above RKV_MAX_LEN), RKV_ERR_WORKSPACE, RKV_ERR_HIP. */
 rkv_status rkv_score(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
@@ -192,7 +229,10 @@ rkv_status rkv_redundancy_gram(const rkv_config *cfg, const rkv_cache *cache, in
                                const int32_t *h_seq_lens, float *redundancy, int32_t stride,
                                void *stream);
 
-/* Step 2, selection: for each triggered unit, keep[0 .. budget-window) = the
+/* Step 2, selection ("How R-KV decides what to drop" on the R-KV project
+ * page: the last window_size tokens stay, the budget bounds what is kept; the
+ * blog's R-KV section: tokens of high importance and low redundancy are the
+ * ones kept): for each triggered unit, keep[0 .. budget-window) = the
  * chosen candidates of [0, len-window) in ascending position order, and
  * keep[budget-window .. budget) = len-window .. len-1 (the window).  Candidates
  * are ranked by score descending, ties by lower position; -0.0 ranks equal to
@@ -200,12 +240,15 @@ rkv_status rkv_redundancy_gram(const rkv_config *cfg, const rkv_cache *cache, in
  * With cfg->shared_selection = 1 the ranking score of a token is the float32
  * sum of its scores over the KV heads of its (sequence, layer), and all those
  * heads receive the same keep row.
- *   scores  device float32 (layout above), as written by rkv_score
- *   keep    device int32 (layout above)
- * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP. */
+ *   scores     device float32 (layout above), as written by rkv_score
+ *   keep       device int32 (layout above)
+ *   workspace  the workspace rkv_score used, or NULL: with a nonzero status
+ *              word the keep rows are not written.  workspace_bytes >= 256.
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP. */
 rkv_status rkv_select(const rkv_config *cfg, int32_t num_seqs, const int32_t *h_seq_lens,
                       const float *scores, int32_t score_stride, int32_t *keep,
-                      void *stream);
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Step 3, compaction and FREE_BLOCKS ("two-phase compaction" and
  * "bounded-footprint block freeing" on the R-KV project page): for each
@@ -219,14 +262,22 @@ rkv_status rkv_select(const rkv_config *cfg, int32_t num_seqs, const int32_t *h_
  * sequences not triggered).  The block table is not modified: returning the
  * ids to an allocator is the caller's.  free_capacity = entries available in
  * free_blocks.  Contiguous layout: free_blocks may be NULL; counts are 0.
- *   keep  device int32 (layout above), ascending per unit, as from rkv_select
+ *   keep       device int32 (layout above), ascending per unit, as from rkv_select
+ *   workspace  the workspace rkv_score used, or NULL.  Given, a nonzero
+ *              status word leaves the cache and free_blocks untouched (the
+ *              host lengths and counts are still updated: after a nonzero
+ *              rkv_device_status the caller restores the lengths it passed).
+ *              With cfg->check_block_table = 1 it is required, and the block
+ *              ids are checked again before the pool is touched.
+ *              workspace_bytes >= 256.
  * Errors: RKV_ERR_INVALID_ARG (including free_capacity too small),
- * RKV_ERR_UNSUPPORTED, RKV_ERR_HIP.  A keep row that is not strictly
- * ascending within [0, len) is undefined behaviour. */
+ * RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE, RKV_ERR_HIP.  A keep row that is
+ * not strictly ascending within [0, len) is undefined behaviour. */
 rkv_status rkv_compact(const rkv_config *cfg, const rkv_cache *cache, int32_t num_seqs,
                        int32_t *h_seq_lens, const int32_t *keep,
                        int32_t *free_blocks, int32_t free_capacity,
-                       int32_t *h_free_counts, void *stream);
+                       int32_t *h_free_counts, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /* The whole step in one call: the outputs of rkv_score (scores only),
  * rkv_select and rkv_compact, with the same arguments and the same results
@@ -235,11 +286,14 @@ rkv_status rkv_compact(const rkv_config *cfg, const rkv_cache *cache, int32_t nu
  * (shared_selection = 0), one kernel per launch
  * scores, selects and compacts each unit, keeping its keys on chip so the
  * keys are read from HBM once; other launches run the three kernels in
- * order (R-KV project page, "How R-KV decides what to drop": the step runs
- * on the critical path, which is why it is fused where it fits).
+ * order (R-KV project page, "How R-KV differs from static KV cache
+ * compression": the scoring work sits on the decode critical path, which is
+ * why it is fused where it fits).
  *   h_seq_lens  host, in/out (triggered sequences become `budget` long)
- *   workspace   as for rkv_score; only launches that cannot run fused use it
- *               (NULL is accepted when every launch runs fused)
+ *   workspace   as for rkv_score; launches that cannot run fused use it for
+ *               their scoring records.  NULL is accepted when every launch
+ *               runs fused and cfg->check_block_table = 0; given, its status
+ *               word is cleared and then set as for the three calls.
  * Errors: the union of those of the three calls. */
 rkv_status rkv_step(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
                     int32_t num_seqs, int32_t *h_seq_lens,
@@ -253,8 +307,9 @@ rkv_status rkv_step(const rkv_config *cfg, const rkv_cache *cache, const void *q
 size_t rkv_step_device_workspace_size(const rkv_config *cfg, int32_t num_seqs, int32_t max_len);
 
 /* rkv_step with the sequence lengths in device memory, for a step that runs
- * inside a captured decode graph (the "in-graph decode" of the R-KV project
- * page's SGLang port, section "How R-KV decides what to drop"): the host
+ * inside a captured decode graph (the in-graph decode the R-KV project page
+ * names for its vLLM port, section "How R-KV differs from static KV cache
+ * compression"): the host
  * takes no decision that depends on the lengths, every launch has a shape
  * fixed by (num_seqs, max_len), and the trigger is taken on the GPU.
  * Results are those of rkv_step for the same lengths, bit for bit.
@@ -271,6 +326,9 @@ size_t rkv_step_device_workspace_size(const rkv_config *cfg, int32_t num_seqs, i
  *   d_free_counts device int32 [num_seqs] or NULL: freed blocks per sequence.
  *   workspace     device, >= rkv_step_device_workspace_size(cfg, num_seqs,
  *                 max_len) bytes, 256-byte aligned; contents on entry ignored.
+ *                 Its status word is set as for rkv_step; a nonzero word
+ *                 leaves the cache, the keep rows and free_blocks untouched
+ *                 (the device lengths and counts are still updated).
  * Errors: those of rkv_step, checked on the host before anything is enqueued
  * (lengths are not read by the host). */
 rkv_status rkv_step_device(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
@@ -278,6 +336,22 @@ rkv_status rkv_step_device(const rkv_config *cfg, const rkv_cache *cache, const 
                            float *scores, int32_t score_stride, int32_t *keep,
                            int32_t *free_blocks, int32_t free_capacity, int32_t *d_free_counts,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* The status word of a workspace (its first 32-bit word) after the calls
+ * enqueued on `stream` so far: waits for the stream, then copies the word to
+ * the host (so it cannot be captured in a graph).  *flags (may be NULL)
+ * receives it: RKV_DEVICE_SPAN_TIMEOUT, RKV_DEVICE_BAD_BLOCK_ID or 0.
+ * Returns RKV_OK for 0, RKV_ERR_DEVICE_CHECK otherwise (the step left the
+ * cache as it was; see rkv_compact for the lengths).
+ * Errors: RKV_ERR_INVALID_ARG (workspace NULL), RKV_ERR_HIP. */
+rkv_status rkv_device_status(const void *workspace, void *stream, uint32_t *flags);
+
+/* Bound of the key-span wait, in microseconds, for launches enqueued after
+ * this call by any thread (default 1000000, at most 60000000).  0 makes every
+ * key span give up at once and report RKV_DEVICE_SPAN_TIMEOUT, which
+ * exercises the failure path.  Returns the previous bound, or -1 (nothing
+ * changed) for an argument outside [0, 60000000]. */
+int64_t rkv_set_span_wait_us(int64_t microseconds);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,10 @@ RKV_ERR_INVALID_ARG = 1
 RKV_ERR_UNSUPPORTED = 2
 RKV_ERR_WORKSPACE = 3
 RKV_ERR_HIP = 4
+RKV_ERR_DEVICE_CHECK = 5
+
+RKV_DEVICE_SPAN_TIMEOUT = 1
+RKV_DEVICE_BAD_BLOCK_ID = 2
 
 RKV_DTYPE_F32 = 0
 RKV_DTYPE_BF16 = 1
@@ -34,18 +38,21 @@ RKV_MAX_WINDOW_ROWS = 142
 EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_workspace_size",
            "rkv_redundancy_gram", "rkv_window_store",
            "rkv_score", "rkv_select", "rkv_compact", "rkv_step",
-           "rkv_step_device_workspace_size", "rkv_step_device")
+           "rkv_step_device_workspace_size", "rkv_step_device", "rkv_device_status",
+           "rkv_set_span_wait_us")
 
 
 class rkv_config(ctypes.Structure):
     _fields_ = [("num_layers", c_int32), ("num_q_heads", c_int32), ("num_kv_heads", c_int32),
                 ("head_dim", c_int32), ("budget", c_int32), ("buffer", c_int32),
                 ("window", c_int32), ("mix_lambda", c_float), ("dtype", c_int32),
-                ("layout", c_int32), ("block_size", c_int32), ("shared_selection", c_int32)]
+                ("layout", c_int32), ("block_size", c_int32), ("shared_selection", c_int32),
+                ("check_block_table", c_int32)]
 
 
 class rkv_cache(ctypes.Structure):
-    _fields_ = [("k", c_void_p), ("v", c_void_p), ("capacity", c_int32),
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("layer_stride", ctypes.c_int64),
+                ("capacity", c_int32),
                 ("num_blocks", c_int32), ("block_table", c_void_p),
                 ("max_blocks_per_seq", c_int32)]
 
@@ -88,10 +95,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_void_p]
     lib.rkv_window_store.restype = c_int32
     lib.rkv_select.argtypes = [P(rkv_config), c_int32, P(c_int32), c_void_p, c_int32, c_void_p,
-                               c_void_p]
+                               c_void_p, c_size_t, c_void_p]
     lib.rkv_select.restype = c_int32
     lib.rkv_compact.argtypes = [P(rkv_config), P(rkv_cache), c_int32, P(c_int32), c_void_p,
-                                c_void_p, c_int32, P(c_int32), c_void_p]
+                                c_void_p, c_int32, P(c_int32), c_void_p, c_size_t, c_void_p]
     lib.rkv_compact.restype = c_int32
     lib.rkv_step.argtypes = [P(rkv_config), P(rkv_cache), c_void_p, c_int32, P(c_int32), c_void_p,
                              c_int32, c_void_p, c_void_p, c_int32, P(c_int32), c_void_p, c_size_t,
@@ -103,6 +110,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                     c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                     c_void_p, c_void_p, c_size_t, c_void_p]
     lib.rkv_step_device.restype = c_int32
+    lib.rkv_device_status.argtypes = [c_void_p, c_void_p, P(ctypes.c_uint32)]
+    lib.rkv_device_status.restype = c_int32
+    lib.rkv_set_span_wait_us.argtypes = [ctypes.c_int64]
+    lib.rkv_set_span_wait_us.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -191,14 +202,17 @@ def rkv_redundancy_gram(cfg, cache, num_seqs, seq_lens, redundancy, stride, stre
                                       _i32p(lens), _ptr(redundancy), stride, _stream(stream)))
 
 
-def rkv_select(cfg, num_seqs, seq_lens, scores, score_stride, keep, stream=None) -> None:
+def rkv_select(cfg, num_seqs, seq_lens, scores, score_stride, keep, workspace=None,
+               workspace_bytes=0, stream=None) -> None:
     lens = _lens(seq_lens)
     _check(load().rkv_select(ctypes.byref(cfg), num_seqs, _i32p(lens), _ptr(scores),
-                             score_stride, _ptr(keep), _stream(stream)))
+                             score_stride, _ptr(keep), _ptr(workspace), workspace_bytes,
+                             _stream(stream)))
 
 
 def rkv_compact(cfg, cache, num_seqs, seq_lens: np.ndarray, keep, free_blocks=None,
-                free_capacity=0, free_counts: Optional[np.ndarray] = None, stream=None) -> None:
+                free_capacity=0, free_counts: Optional[np.ndarray] = None, workspace=None,
+                workspace_bytes=0, stream=None) -> None:
     """seq_lens must be a C-contiguous int32 numpy array: it is updated in place
     (triggered sequences become `budget` long).  free_counts likewise."""
     if not (isinstance(seq_lens, np.ndarray) and seq_lens.dtype == np.int32
@@ -209,7 +223,7 @@ def rkv_compact(cfg, cache, num_seqs, seq_lens: np.ndarray, keep, free_blocks=No
         raise TypeError("free_counts must be a C-contiguous int32 numpy array")
     _check(load().rkv_compact(ctypes.byref(cfg), ctypes.byref(cache), num_seqs, _i32p(seq_lens),
                               _ptr(keep), _ptr(free_blocks), free_capacity, _i32p(free_counts),
-                              _stream(stream)))
+                              _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def rkv_step(cfg, cache, q_window, num_seqs, seq_lens: np.ndarray, scores, score_stride, keep,
@@ -244,16 +258,32 @@ def rkv_step_device(cfg, cache, q_window, num_seqs, d_seq_lens, max_len, scores,
                                   _stream(stream)))
 
 
+def rkv_device_status(workspace, stream=None) -> int:
+    """The workspace's status word (waits for the stream): 0, or the
+    RKV_DEVICE_* flags of the checks that failed.  Other errors raise."""
+    flags = ctypes.c_uint32(0)
+    st = load().rkv_device_status(_ptr(workspace), _stream(stream), ctypes.byref(flags))
+    if st not in (RKV_OK, RKV_ERR_DEVICE_CHECK):
+        _check(st)
+    return int(flags.value)
+
+
+def rkv_set_span_wait_us(microseconds: int) -> int:
+    return int(load().rkv_set_span_wait_us(microseconds))
+
+
 # ------------------------------------------------------------------ helpers
 
 def make_config(num_layers, num_q_heads, num_kv_heads, head_dim, budget, buffer, window,
                 mix_lambda, dtype="bf16", layout="contiguous", block_size=16,
-                shared_selection=False) -> rkv_config:
+                shared_selection=False, check_block_table=False) -> rkv_config:
     return rkv_config(num_layers, num_q_heads, num_kv_heads, head_dim, budget, buffer, window,
                       mix_lambda, RKV_DTYPE_BF16 if dtype == "bf16" else RKV_DTYPE_F32,
                       RKV_LAYOUT_PAGED if layout == "paged" else RKV_LAYOUT_CONTIGUOUS,
-                      block_size, 1 if shared_selection else 0)
+                      block_size, 1 if shared_selection else 0, 1 if check_block_table else 0)
 
 
-def make_cache(k, v, capacity=0, num_blocks=0, block_table=None, max_blocks_per_seq=0) -> rkv_cache:
-    return rkv_cache(_ptr(k), _ptr(v), capacity, num_blocks, _ptr(block_table), max_blocks_per_seq)
+def make_cache(k, v, capacity=0, num_blocks=0, block_table=None, max_blocks_per_seq=0,
+               layer_stride=0) -> rkv_cache:
+    return rkv_cache(_ptr(k), _ptr(v), layer_stride, capacity, num_blocks, _ptr(block_table),
+                     max_blocks_per_seq)

@@ -32,6 +32,15 @@ rkv_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+// Every workspace starts with this many bytes holding the status word.
+constexpr size_t kStatusBytes = 256;
+
+uint32_t* status_of(void* ws) { return static_cast<uint32_t*>(ws); }
+float* records_of(void* ws) {
+  return reinterpret_cast<float*>(static_cast<char*>(ws) + kStatusBytes);
+}
 
 int ilog2_exact(int v) {
   if (v < 1 || (v & (v - 1)) != 0) return -1;
@@ -72,10 +81,24 @@ rkv_status check_config(const rkv_config* c) {
     return fail(RKV_ERR_UNSUPPORTED, "budget %d exceeds %d", c->budget, RKV_MAX_LEN);
   if (c->shared_selection != 0 && c->shared_selection != 1)
     return fail(RKV_ERR_INVALID_ARG, "shared_selection must be 0 or 1");
+  if (c->check_block_table != 0 && c->check_block_table != 1)
+    return fail(RKV_ERR_INVALID_ARG, "check_block_table must be 0 or 1");
   return RKV_OK;
 }
 
-rkv_status check_cache(const rkv_config* c, const rkv_cache* k, bool need_v) {
+// True if the call checks block ids on the device (paged layout only).
+bool checks_blocks(const rkv_config* c) {
+  return c->layout == RKV_LAYOUT_PAGED && c->check_block_table == 1;
+}
+
+// Elements of one layer of K (or V) when packed.
+int64_t packed_layer(const rkv_config* c, const rkv_cache* k, int32_t num_seqs) {
+  if (c->layout == RKV_LAYOUT_CONTIGUOUS)
+    return (int64_t)num_seqs * c->num_kv_heads * k->capacity * c->head_dim;
+  return (int64_t)k->num_blocks * c->num_kv_heads * c->block_size * c->head_dim;
+}
+
+rkv_status check_cache(const rkv_config* c, const rkv_cache* k, bool need_v, int32_t num_seqs) {
   if (k == nullptr) return fail(RKV_ERR_INVALID_ARG, "cache is NULL");
   if (k->k == nullptr) return fail(RKV_ERR_INVALID_ARG, "cache->k is NULL");
   if (need_v && k->v == nullptr) return fail(RKV_ERR_INVALID_ARG, "cache->v is NULL");
@@ -88,6 +111,15 @@ rkv_status check_cache(const rkv_config* c, const rkv_cache* k, bool need_v) {
     if (k->block_table == nullptr) return fail(RKV_ERR_INVALID_ARG, "block_table is NULL");
     if (k->max_blocks_per_seq < 1) return fail(RKV_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
   }
+  if (k->layer_stride < 0) return fail(RKV_ERR_INVALID_ARG, "layer_stride must be >= 0");
+  const int64_t esize = c->dtype == RKV_DTYPE_BF16 ? 2 : 4;
+  if (k->layer_stride != 0 && (k->layer_stride * esize) % 16 != 0)
+    return fail(RKV_ERR_INVALID_ARG, "layer_stride of %lld elements is not a multiple of 16 bytes",
+                (long long)k->layer_stride);
+  const int64_t packed = packed_layer(c, k, num_seqs < 0 ? 0 : num_seqs);
+  if (k->layer_stride != 0 && c->num_layers > 1 && k->layer_stride < packed)
+    return fail(RKV_ERR_INVALID_ARG, "layer_stride %lld is below the %lld elements of one layer",
+                (long long)k->layer_stride, (long long)packed);
   return RKV_OK;
 }
 
@@ -137,6 +169,7 @@ rkv::Geom make_geom(const rkv_config* c, const rkv_cache* cache, int32_t num_seq
     g.cap = cache->capacity;
     g.nblk = cache->num_blocks;
     g.maxblk = cache->max_blocks_per_seq;
+    g.layer_stride = cache->layer_stride != 0 ? cache->layer_stride : packed_layer(c, cache, num_seqs);
   }
   g.bs_shift = g.paged ? ilog2_exact(c->block_size) : 0;
   g.shared = c->shared_selection;
@@ -167,7 +200,7 @@ size_t ws_bytes_for(const rkv_config* c, long seqs, long max_len) {
   const long t = std::min<long>(seqs, rkv::kMaxTrig);
   const long chunks = (max_len + rkv::kChunk - 1) / rkv::kChunk;
   const size_t bytes = (size_t)t * c->num_layers * c->num_kv_heads * chunks * record_floats(c) * 4;
-  return (bytes + 255) & ~(size_t)255;
+  return kStatusBytes + ((bytes + 255) & ~(size_t)255);
 }
 
 rkv::ScoreArgs make_score_args(const rkv_config* cfg, const rkv_cache* cache, const void* q,
@@ -181,7 +214,8 @@ rkv::ScoreArgs make_score_args(const rkv_config* cfg, const rkv_cache* cache, co
   a.scores = scores;
   a.imp = imp;
   a.red = red;
-  a.part = static_cast<float*>(workspace);
+  a.part = workspace != nullptr ? records_of(workspace) : nullptr;
+  a.status = workspace != nullptr ? status_of(workspace) : nullptr;
   a.score_stride = score_stride;
   a.gw = a.g.group * cfg->window;
   a.rec = (int32_t)record_floats(cfg);
@@ -214,8 +248,8 @@ rkv_status free_block_plan(const rkv_config* cfg, int32_t num_seqs, const std::v
   return RKV_OK;
 }
 
-// Device path (rkv_step_device): the table sits at the start of the
-// workspace, the scoring records after it.
+// Device path (rkv_step_device): the status word, then the table, then the
+// scoring records.
 size_t dev_table_bytes(long seqs) { return ((size_t)(1 + 3 * seqs) * 4 + 255) & ~(size_t)255; }
 
 size_t dev_records_bytes(const rkv_config* c, long seqs, long max_len) {
@@ -235,6 +269,161 @@ bool dev_fusable(const rkv_config* c, int32_t max_len) {
 
 }  // namespace
 
+
+namespace {
+
+rkv_status check_ws(const void* ws, size_t bytes, size_t need) {
+  if (ws == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned256(ws)) return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < need) return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", bytes, need);
+  return RKV_OK;
+}
+
+// The prologue of one launch's triggered rows: clear the status word
+// (reset), check their block ids (check).
+hipError_t prologue(const rkv::Geom& g, const rkv::TrigTable& tt, void* ws, const rkv_cache* cache,
+                    bool reset, bool check, hipStream_t hs) {
+  rkv::PrologueArgs p{};
+  p.g = g;
+  p.tt = tt;
+  p.status = status_of(ws);
+  p.bt = check ? cache->block_table : nullptr;
+  p.reset = reset ? 1 : 0;
+  return rkv::launch_prologue(p, hs);
+}
+
+// rkv_step (also behind the allocation-free entry point).  Launches of at
+// most kMaxTrig sequences each; those that cannot run fused score, then
+// select, then compact -- scoring of all of them first, so that a device
+// check failing in any of them stops every write of the call -- and the
+// fused launches come last.
+rkv_status step_impl(const rkv_config* cfg, const rkv_cache* cache, const void* q_window,
+                     int32_t num_seqs, int32_t* h_seq_lens, float* scores, int32_t score_stride,
+                     int32_t* keep, int32_t* free_blocks, int32_t free_capacity,
+                     int32_t* h_free_counts, void* workspace, size_t workspace_bytes,
+                     hipStream_t hs) {
+  rkv_status st = check_config(cfg);
+  if (st != RKV_OK) return st;
+  std::vector<Trig> trig;
+  if ((st = check_cache(cfg, cache, true, num_seqs)) != RKV_OK) return st;
+  if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
+  std::vector<int32_t> counts, offs;
+  if ((st = free_block_plan(cfg, num_seqs, trig, free_blocks, free_capacity, counts, offs)) != RKV_OK)
+    return st;
+  const bool bf16 = cfg->dtype == RKV_DTYPE_BF16;
+  const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
+  const bool check = checks_blocks(cfg);
+  if (!trig.empty()) {
+    if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
+    if (!aligned16(q_window)) return fail(RKV_ERR_INVALID_ARG, "q_window must be 16-byte aligned");
+    if (scores == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores is NULL");
+    if (keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
+    const int32_t maxn = max_len_of(trig, 0, trig.size());
+    if (score_stride < maxn)
+      return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
+                  score_stride, maxn);
+    rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
+                                       nullptr, nullptr, workspace);
+    struct Launch {
+      size_t first;
+      int cnt, max_len;
+      bool fused;
+    };
+    std::vector<Launch> plan;
+    bool any_unfused = false;
+    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+      const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+      a.max_len = max_len_of(trig, first, cnt);
+      const bool fused = rkv::step_fusable(a, bf16);
+      plan.push_back({first, cnt, a.max_len, fused});
+      if (fused) continue;
+      any_unfused = true;
+      // launches that cannot run fused need the scoring workspace
+      if ((st = check_ws(workspace, workspace_bytes, ws_bytes_for(cfg, cnt, a.max_len))) != RKV_OK)
+        return st;
+    }
+    if (check && workspace == nullptr)
+      return fail(RKV_ERR_WORKSPACE, "check_block_table needs a workspace");
+    if (workspace != nullptr && (st = check_ws(workspace, workspace_bytes, kStatusBytes)) != RKV_OK)
+      return st;
+    {
+      const hipError_t e = rkv::prepare_select();
+      if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
+    }
+    hipError_t e;
+    const bool pro = workspace != nullptr && (any_unfused || check);
+    if (pro) {
+      for (size_t i = 0; i < plan.size(); ++i) {
+        fill_table(a.tt, trig, plan[i].first, plan[i].cnt, nullptr);
+        a.g.num_trig = plan[i].cnt;
+        if ((e = prologue(a.g, a.tt, workspace, cache, i == 0, check, hs)) != hipSuccess)
+          return hip_fail(e, "prologue launch");
+      }
+    }
+    auto set_launch = [&](const Launch& p) {
+      fill_table(a.tt, trig, p.first, p.cnt, offs.data());
+      a.g.num_trig = p.cnt;
+      a.max_len = p.max_len;
+      a.max_chunks = (a.max_len + rkv::kChunk - 1) / rkv::kChunk;
+    };
+    for (const Launch& p : plan) {
+      if (p.fused) continue;
+      set_launch(p);
+      if ((e = rkv::launch_score(a, bf16, hs)) != hipSuccess) return hip_fail(e, "score launch");
+    }
+    for (const Launch& p : plan) {
+      if (p.fused) continue;
+      set_launch(p);
+      rkv::SelectArgs sl{};
+      sl.g = a.g;
+      sl.tt = a.tt;
+      sl.scores = scores;
+      sl.keep = keep;
+      sl.score_stride = score_stride;
+      sl.status = a.status;
+      if ((e = rkv::launch_select(sl, a.max_len, hs)) != hipSuccess) return hip_fail(e, "select launch");
+    }
+    for (const Launch& p : plan) {
+      if (p.fused) continue;
+      set_launch(p);
+      rkv::CompactArgs ca{};
+      ca.g = a.g;
+      ca.tt = a.tt;
+      ca.k = cache->k;
+      ca.v = cache->v;
+      ca.bt = cache->block_table;
+      ca.keep = keep;
+      ca.free_blocks = paged ? free_blocks : nullptr;
+      ca.row_bytes = cfg->head_dim * (bf16 ? 2 : 4);
+      ca.status = a.status;
+      if ((e = rkv::launch_compact(ca, hs)) != hipSuccess) return hip_fail(e, "compact launch");
+    }
+    // fused launches: after a prologue they check the status word; without
+    // one the first of them clears it
+    bool reset_pending = workspace != nullptr && !pro;
+    for (const Launch& p : plan) {
+      if (!p.fused) continue;
+      set_launch(p);
+      rkv::StepArgs sa{};
+      sa.s = a;
+      sa.s.status = pro || reset_pending ? status_of(workspace) : nullptr;
+      sa.reset_status = reset_pending ? 1 : 0;
+      reset_pending = false;
+      sa.k = cache->k;
+      sa.v = cache->v;
+      sa.keep = keep;
+      sa.free_blocks = paged ? free_blocks : nullptr;
+      if ((e = rkv::launch_step(sa, hs)) != hipSuccess) return hip_fail(e, "step launch");
+    }
+  }
+  for (const Trig& t : trig) h_seq_lens[t.seq] = cfg->budget;
+  if (h_free_counts != nullptr)
+    for (int32_t s = 0; s < num_seqs; ++s) h_free_counts[s] = counts[s];
+  return RKV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* rkv_status_string(rkv_status s) {
@@ -244,6 +433,7 @@ const char* rkv_status_string(rkv_status s) {
     case RKV_ERR_UNSUPPORTED: return "RKV_ERR_UNSUPPORTED";
     case RKV_ERR_WORKSPACE: return "RKV_ERR_WORKSPACE";
     case RKV_ERR_HIP: return "RKV_ERR_HIP";
+    case RKV_ERR_DEVICE_CHECK: return "RKV_ERR_DEVICE_CHECK";
   }
   return "RKV_ERR_UNKNOWN";
 }
@@ -268,7 +458,7 @@ rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* 
   rkv_status st = check_config(cfg);
   if (st != RKV_OK) return st;
   std::vector<Trig> trig;
-  if ((st = check_cache(cfg, cache, false)) != RKV_OK) return st;
+  if ((st = check_cache(cfg, cache, false, num_seqs)) != RKV_OK) return st;
   if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
   if (trig.empty()) return RKV_OK;
   if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
@@ -278,26 +468,25 @@ rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* 
   if (score_stride < maxn)
     return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
                 score_stride, maxn);
-  if (workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
     const size_t cnt = std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
     const size_t need = ws_bytes_for(cfg, (long)cnt, max_len_of(trig, first, cnt));
-    if (workspace_bytes < need)
-      return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if ((st = check_ws(workspace, workspace_bytes, need)) != RKV_OK) return st;
   }
 
   rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
                                      importance, redundancy, workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool check = checks_blocks(cfg);
   for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
     const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
     fill_table(a.tt, trig, first, cnt, nullptr);
     a.g.num_trig = cnt;
     a.max_len = max_len_of(trig, first, cnt);
     a.max_chunks = (a.max_len + rkv::kChunk - 1) / rkv::kChunk;
-    hipError_t e = rkv::launch_score(a, cfg->dtype == RKV_DTYPE_BF16, hs);
+    hipError_t e = prologue(a.g, a.tt, workspace, cache, first == 0, check, hs);
+    if (e != hipSuccess) return hip_fail(e, "prologue launch");
+    e = rkv::launch_score(a, cfg->dtype == RKV_DTYPE_BF16, hs);
     if (e != hipSuccess) return hip_fail(e, "score launch");
   }
   return RKV_OK;
@@ -346,7 +535,7 @@ rkv_status rkv_redundancy_gram(const rkv_config* cfg, const rkv_cache* cache, in
   if (cfg->dtype != RKV_DTYPE_BF16)
     return fail(RKV_ERR_UNSUPPORTED, "rkv_redundancy_gram takes bf16 caches");
   std::vector<Trig> trig;
-  if ((st = check_cache(cfg, cache, false)) != RKV_OK) return st;
+  if ((st = check_cache(cfg, cache, false, num_seqs)) != RKV_OK) return st;
   if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
   if (trig.empty()) return RKV_OK;
   if (redundancy == nullptr) return fail(RKV_ERR_INVALID_ARG, "redundancy is NULL");
@@ -376,7 +565,8 @@ rkv_status rkv_redundancy_gram(const rkv_config* cfg, const rkv_cache* cache, in
 }
 
 rkv_status rkv_select(const rkv_config* cfg, int32_t num_seqs, const int32_t* h_seq_lens,
-                      const float* scores, int32_t score_stride, int32_t* keep, void* stream) {
+                      const float* scores, int32_t score_stride, int32_t* keep, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   g_err.clear();
   rkv_status st = check_config(cfg);
   if (st != RKV_OK) return st;
@@ -389,6 +579,8 @@ rkv_status rkv_select(const rkv_config* cfg, int32_t num_seqs, const int32_t* h_
   if (score_stride < maxn)
     return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
                 score_stride, maxn);
+  if (workspace != nullptr && (st = check_ws(workspace, workspace_bytes, kStatusBytes)) != RKV_OK)
+    return st;
   {
     hipError_t e = rkv::prepare_select();
     if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
@@ -398,6 +590,7 @@ rkv_status rkv_select(const rkv_config* cfg, int32_t num_seqs, const int32_t* h_
   a.scores = scores;
   a.keep = keep;
   a.score_stride = score_stride;
+  a.status = workspace != nullptr ? status_of(workspace) : nullptr;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
     const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
@@ -411,18 +604,24 @@ rkv_status rkv_select(const rkv_config* cfg, int32_t num_seqs, const int32_t* h_
 
 rkv_status rkv_compact(const rkv_config* cfg, const rkv_cache* cache, int32_t num_seqs,
                        int32_t* h_seq_lens, const int32_t* keep, int32_t* free_blocks,
-                       int32_t free_capacity, int32_t* h_free_counts, void* stream) {
+                       int32_t free_capacity, int32_t* h_free_counts, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   g_err.clear();
   rkv_status st = check_config(cfg);
   if (st != RKV_OK) return st;
   std::vector<Trig> trig;
-  if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
+  if ((st = check_cache(cfg, cache, true, num_seqs)) != RKV_OK) return st;
   if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
   const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
+  const bool check = checks_blocks(cfg);
   std::vector<int32_t> counts, offs;
   if ((st = free_block_plan(cfg, num_seqs, trig, free_blocks, free_capacity, counts, offs)) != RKV_OK)
     return st;
   if (!trig.empty() && keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
+  if (!trig.empty() && check && workspace == nullptr)
+    return fail(RKV_ERR_WORKSPACE, "check_block_table needs a workspace");
+  if (workspace != nullptr && (st = check_ws(workspace, workspace_bytes, kStatusBytes)) != RKV_OK)
+    return st;
   if (!trig.empty()) {
     rkv::CompactArgs a{};
     a.g = make_geom(cfg, cache, num_seqs);
@@ -432,12 +631,16 @@ rkv_status rkv_compact(const rkv_config* cfg, const rkv_cache* cache, int32_t nu
     a.keep = keep;
     a.free_blocks = paged ? free_blocks : nullptr;
     a.row_bytes = cfg->head_dim * (cfg->dtype == RKV_DTYPE_BF16 ? 2 : 4);
+    a.status = workspace != nullptr ? status_of(workspace) : nullptr;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
       const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
       fill_table(a.tt, trig, first, cnt, offs.data());
       a.g.num_trig = cnt;
-      hipError_t e = rkv::launch_compact(a, hs);
+      hipError_t e;
+      if (check && (e = prologue(a.g, a.tt, workspace, cache, false, true, hs)) != hipSuccess)
+        return hip_fail(e, "prologue launch");
+      e = rkv::launch_compact(a, hs);
       if (e != hipSuccess) return hip_fail(e, "compact launch");
     }
   }
@@ -452,94 +655,14 @@ rkv_status rkv_step(const rkv_config* cfg, const rkv_cache* cache, const void* q
                     int32_t* keep, int32_t* free_blocks, int32_t free_capacity,
                     int32_t* h_free_counts, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
-  rkv_status st = check_config(cfg);
-  if (st != RKV_OK) return st;
-  std::vector<Trig> trig;
-  if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
-  if ((st = collect(cfg, cache, num_seqs, h_seq_lens, trig)) != RKV_OK) return st;
-  std::vector<int32_t> counts, offs;
-  if ((st = free_block_plan(cfg, num_seqs, trig, free_blocks, free_capacity, counts, offs)) != RKV_OK)
-    return st;
-  const bool bf16 = cfg->dtype == RKV_DTYPE_BF16;
-  const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
-  if (!trig.empty()) {
-    if (q_window == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_window is NULL");
-    if (!aligned16(q_window)) return fail(RKV_ERR_INVALID_ARG, "q_window must be 16-byte aligned");
-    if (scores == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores is NULL");
-    if (keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "keep is NULL");
-    const int32_t maxn = max_len_of(trig, 0, trig.size());
-    if (score_stride < maxn)
-      return fail(RKV_ERR_INVALID_ARG, "score_stride %d is below the longest triggered length %d",
-                  score_stride, maxn);
-    rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
-                                       nullptr, nullptr, workspace);
-    // launches that cannot run fused need the scoring workspace: check them all first
-    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
-      const size_t cnt = std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
-      a.max_len = max_len_of(trig, first, cnt);
-      if (rkv::step_fusable(a, bf16)) continue;
-      if (workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
-      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-      const size_t need = ws_bytes_for(cfg, (long)cnt, a.max_len);
-      if (workspace_bytes < need)
-        return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-    }
-    {
-      const hipError_t e = rkv::prepare_select();
-      if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
-    }
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
-      const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
-      fill_table(a.tt, trig, first, cnt, offs.data());
-      a.g.num_trig = cnt;
-      a.max_len = max_len_of(trig, first, cnt);
-      a.max_chunks = (a.max_len + rkv::kChunk - 1) / rkv::kChunk;
-      hipError_t e;
-      if (rkv::step_fusable(a, bf16)) {
-        rkv::StepArgs sa{};
-        sa.s = a;
-        sa.k = cache->k;
-        sa.v = cache->v;
-        sa.keep = keep;
-        sa.free_blocks = paged ? free_blocks : nullptr;
-        e = rkv::launch_step(sa, hs);
-        if (e != hipSuccess) return hip_fail(e, "step launch");
-        continue;
-      }
-      e = rkv::launch_score(a, bf16, hs);
-      if (e != hipSuccess) return hip_fail(e, "score launch");
-      rkv::SelectArgs sl{};
-      sl.g = a.g;
-      sl.tt = a.tt;
-      sl.scores = scores;
-      sl.keep = keep;
-      sl.score_stride = score_stride;
-      e = rkv::launch_select(sl, a.max_len, hs);
-      if (e != hipSuccess) return hip_fail(e, "select launch");
-      rkv::CompactArgs ca{};
-      ca.g = a.g;
-      ca.tt = a.tt;
-      ca.k = cache->k;
-      ca.v = cache->v;
-      ca.bt = cache->block_table;
-      ca.keep = keep;
-      ca.free_blocks = paged ? free_blocks : nullptr;
-      ca.row_bytes = cfg->head_dim * (bf16 ? 2 : 4);
-      e = rkv::launch_compact(ca, hs);
-      if (e != hipSuccess) return hip_fail(e, "compact launch");
-    }
-  }
-  for (const Trig& t : trig) h_seq_lens[t.seq] = cfg->budget;
-  if (h_free_counts != nullptr)
-    for (int32_t s = 0; s < num_seqs; ++s) h_free_counts[s] = counts[s];
-  return RKV_OK;
+  return step_impl(cfg, cache, q_window, num_seqs, h_seq_lens, scores, score_stride, keep,
+                   free_blocks, free_capacity, h_free_counts, workspace, workspace_bytes,
+                   static_cast<hipStream_t>(stream));
 }
 
 size_t rkv_step_device_workspace_size(const rkv_config* cfg, int32_t num_seqs, int32_t max_len) {
   if (check_config(cfg) != RKV_OK || num_seqs < 0 || max_len < 0 || max_len > RKV_MAX_LEN) return 0;
-  size_t b = dev_table_bytes(num_seqs);
+  size_t b = kStatusBytes + dev_table_bytes(num_seqs);
   if (!dev_fusable(cfg, max_len)) b += dev_records_bytes(cfg, num_seqs, max_len);
   return b;
 }
@@ -552,7 +675,7 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
   g_err.clear();
   rkv_status st = check_config(cfg);
   if (st != RKV_OK) return st;
-  if ((st = check_cache(cfg, cache, true)) != RKV_OK) return st;
+  if ((st = check_cache(cfg, cache, true, num_seqs)) != RKV_OK) return st;
   if (num_seqs < 0) return fail(RKV_ERR_INVALID_ARG, "num_seqs must be >= 0");
   if (num_seqs == 0) return RKV_OK;
   if (d_seq_lens == nullptr) return fail(RKV_ERR_INVALID_ARG, "d_seq_lens is NULL");
@@ -581,18 +704,15 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
       return fail(RKV_ERR_INVALID_ARG, "free_capacity %d below the %ld entries of the worst case",
                   free_capacity, need);
   }
-  if (workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "workspace is NULL");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(RKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const size_t need = rkv_step_device_workspace_size(cfg, num_seqs, max_len);
-  if (workspace_bytes < need)
-    return fail(RKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if ((st = check_ws(workspace, workspace_bytes,
+                     rkv_step_device_workspace_size(cfg, num_seqs, max_len))) != RKV_OK)
+    return st;
   {
     const hipError_t e = rkv::prepare_select();
     if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
   }
 
-  int32_t* dtab = static_cast<int32_t*>(workspace);
+  int32_t* dtab = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kStatusBytes);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   rkv::TableArgs ta{};
   ta.lens = d_seq_lens;
@@ -603,20 +723,24 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
   ta.trigger = cfg->budget + cfg->buffer;
   ta.max_len = max_len;
   ta.block_size = paged ? cfg->block_size : 0;
+  ta.status = status_of(workspace);
+  ta.bt = checks_blocks(cfg) ? cache->block_table : nullptr;
+  ta.maxblk = cache->max_blocks_per_seq;
+  ta.nblk = cache->num_blocks;
   hipError_t e = rkv::launch_table(ta, hs);
   if (e != hipSuccess) return hip_fail(e, "table launch");
   if (max_len < (long)cfg->budget + cfg->buffer) return RKV_OK;   // nothing can trigger
 
-  float* records = reinterpret_cast<float*>(static_cast<char*>(workspace) + dev_table_bytes(num_seqs));
   rkv::ScoreArgs a = make_score_args(cfg, cache, q_window, num_seqs, scores, score_stride,
-                                     nullptr, nullptr, records);
+                                     nullptr, nullptr, workspace);
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(dtab) + dev_table_bytes(num_seqs));
   a.g.num_trig = num_seqs;
   a.g.dtab = dtab;
   a.max_len = max_len;
   a.max_chunks = (max_len + rkv::kChunk - 1) / rkv::kChunk;
   if (rkv::step_fusable(a, bf16)) {
     rkv::StepArgs sa{};
-    sa.s = a;
+    sa.s = a;   // status checked: the table kernel cleared and set it
     sa.k = cache->k;
     sa.v = cache->v;
     sa.keep = keep;
@@ -632,6 +756,7 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
   sl.scores = scores;
   sl.keep = keep;
   sl.score_stride = score_stride;
+  sl.status = a.status;
   e = rkv::launch_select(sl, max_len, hs);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   rkv::CompactArgs ca{};
@@ -642,9 +767,32 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
   ca.keep = keep;
   ca.free_blocks = paged ? free_blocks : nullptr;
   ca.row_bytes = cfg->head_dim * (bf16 ? 2 : 4);
+  ca.status = a.status;
   e = rkv::launch_compact(ca, hs);
   if (e != hipSuccess) return hip_fail(e, "compact launch");
   return RKV_OK;
+}
+
+rkv_status rkv_device_status(const void* workspace, void* stream, uint32_t* flags) {
+  g_err.clear();
+  if (workspace == nullptr) return fail(RKV_ERR_INVALID_ARG, "workspace is NULL");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e, "status read");
+  if (flags != nullptr) *flags = word;
+  if (word == 0) return RKV_OK;
+  return fail(RKV_ERR_DEVICE_CHECK, "device check failed (flags 0x%x:%s%s); the cache was left as it was",
+              word, (word & RKV_DEVICE_SPAN_TIMEOUT) ? " key-span wait timed out" : "",
+              (word & RKV_DEVICE_BAD_BLOCK_ID) ? " block id outside the pool" : "");
+}
+
+int64_t rkv_set_span_wait_us(int64_t microseconds) {
+  if (microseconds < 0 || microseconds > 60000000) return -1;
+  const int64_t prev = rkv::span_wait_ticks() / 100;
+  rkv::set_span_wait_ticks(microseconds * 100);   // s_memrealtime: 100 MHz
+  return prev;
 }
 
 }  // extern "C"

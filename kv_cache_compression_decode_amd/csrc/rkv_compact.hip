@@ -23,14 +23,15 @@ namespace rkv {
 namespace {
 constexpr int kCompactRows = 8;   // rows per thread per tile (named registers below)
 
+// Element offset of token t's row; base = head_base of the unit.
 template <bool PAGED>
-__device__ __forceinline__ int64_t row_at(const CompactArgs& a, const Unit& u, int t) {
+__device__ __forceinline__ int64_t row_at(const CompactArgs& a, const Unit& u, int64_t base, int t) {
   if constexpr (PAGED) {
     const int blk = a.bt[(int64_t)u.s * a.g.maxblk + (t >> a.g.bs_shift)];
-    const int bs = 1 << a.g.bs_shift;
-    return ((((int64_t)u.l * a.g.nblk + blk) * a.g.hkv + u.h) * bs + (t & (bs - 1))) * a.g.d;
+    const int64_t blk_stride = ((int64_t)a.g.hkv << a.g.bs_shift) * a.g.d;
+    return base + blk * blk_stride + (int64_t)(t & ((1 << a.g.bs_shift) - 1)) * a.g.d;
   } else {
-    return ((((int64_t)u.l * a.g.num_seqs + u.s) * a.g.hkv + u.h) * a.g.cap + t) * a.g.d;
+    return base + (int64_t)t * a.g.d;
   }
 }
 
@@ -50,7 +51,9 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int unit_id = blockIdx.x / (2 * PARTS);
   const Unit u = decode_unit(a.g, a.tt, unit_id);
   if (u.n == 0) return;   // past the device table's count
+  if (step_aborted(a.status)) return;   // the step failed a device check: cache untouched
   const int tid = threadIdx.x;
+  const int64_t hb = head_base(a.g, u.l, u.s, u.h);
   const int budget = a.g.budget;
   const int esize = a.row_bytes / a.g.d;
   uint8_t* base = reinterpret_cast<uint8_t*>(which ? a.v : a.k) + part * (TPR * 16) +
@@ -77,8 +80,8 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
 #define RKV_LOAD(r)                                                                  \
     const int s##r = min(t0 + r * RPP + rr, budget - 1);                             \
     const uint4 b##r = stream_load(reinterpret_cast<const uint4*>(                   \
-        base + row_at<PAGED>(a, u, keep_s[s##r]) * esize));
-#define RKV_STORE(r) stream_store(reinterpret_cast<uint4*>(base + row_at<PAGED>(a, u, s##r) * esize), b##r);
+        base + row_at<PAGED>(a, u, hb, keep_s[s##r]) * esize));
+#define RKV_STORE(r) stream_store(reinterpret_cast<uint4*>(base + row_at<PAGED>(a, u, hb, s##r) * esize), b##r);
     RKV_LOAD(0) RKV_LOAD(1) RKV_LOAD(2) RKV_LOAD(3) RKV_LOAD(4) RKV_LOAD(5) RKV_LOAD(6) RKV_LOAD(7)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

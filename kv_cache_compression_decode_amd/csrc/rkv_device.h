@@ -35,6 +35,7 @@ struct Geom {
   int32_t nblk, maxblk;        // paged: pool blocks per layer, table row length
   int32_t num_trig;            // triggered sequences in this launch (device table: num_seqs)
   int32_t shared;              // 1: one keep set per (sequence, layer), from the summed scores
+  int64_t layer_stride;        // elements from layer l to l + 1 of K and of V
   // Device-resident table of triggered sequences (rkv_step_device), or null
   // for the by-value TrigTable: [count][seq x num_seqs][len x num_seqs]
   // [free_off x num_seqs]; launches cover num_seqs sequences and the units of
@@ -70,14 +71,25 @@ __device__ __forceinline__ void lds_max(uint32_t* p, uint32_t v) {
   asm volatile("ds_max_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
 
-// Element offset of the row of token t of (layer l, sequence s, kv head h).
-__device__ __forceinline__ int64_t row_offset(const Geom& g, const int32_t* __restrict__ bt,
-                                              int l, int s, int h, int t) {
-  if (!g.paged)
-    return ((((int64_t)l * g.num_seqs + s) * g.hkv + h) * g.cap + t) * g.d;
-  const int blk = bt[(int64_t)s * g.maxblk + (t >> g.bs_shift)];
-  const int bs = 1 << g.bs_shift;
-  return ((((int64_t)l * g.nblk + blk) * g.hkv + h) * bs + (t & (bs - 1))) * g.d;
+// Status word flags, as in rkv.h: set on the device, read back by
+// rkv_device_status.
+constexpr uint32_t kSpanTimeout = RKV_DEVICE_SPAN_TIMEOUT;
+constexpr uint32_t kBadBlockId = RKV_DEVICE_BAD_BLOCK_ID;
+
+// True if a kernel of the step must leave everything untouched: the status
+// word (when the call has one) holds one of the flags in mask.  The word is
+// written only by kernels that run before the reader on the same stream, or
+// -- the span-timeout flag -- by key-span launches, which therefore test
+// only kBadBlockId.
+__device__ __forceinline__ bool step_aborted(const uint32_t* status, uint32_t mask = ~0u) {
+  return status != nullptr && (*status & mask) != 0u;
+}
+
+// Element offset of (layer l, kv head h)'s row 0 in a contiguous cache
+// (sequence s) or in physical block 0 of a paged pool (s unused).
+__device__ __forceinline__ int64_t head_base(const Geom& g, int l, int s, int h) {
+  if (!g.paged) return l * g.layer_stride + (((int64_t)s * g.hkv + h) * g.cap) * g.d;
+  return l * g.layer_stride + ((int64_t)h << g.bs_shift) * g.d;
 }
 
 // Units are (triggered sequence, layer, kv head), kv head fastest.

@@ -25,6 +25,10 @@ struct ScoreArgs {
   int32_t rec;            // floats per chunk record: 2 * gw + d
   float lambda;
   float c;                // log2(e) / sqrt(d): raw dot -> log2-scaled logit
+  // Status word of the call's workspace, or nullptr.  Scoring kernels return
+  // at once if it holds kBadBlockId (the pool must not be read); key-span
+  // launches set kSpanTimeout in it.
+  uint32_t* status;
 };
 
 struct SelectArgs {
@@ -33,6 +37,7 @@ struct SelectArgs {
   const float* scores;
   int32_t* keep;          // [L][S][Hkv][budget]
   int32_t score_stride;
+  const uint32_t* status; // nonzero word: write nothing (nullptr: no check)
 };
 
 struct CompactArgs {
@@ -44,6 +49,7 @@ struct CompactArgs {
   const int32_t* keep;
   int32_t* free_blocks;   // paged FREE_BLOCKS output or nullptr
   int32_t row_bytes;      // d * element size
+  const uint32_t* status; // nonzero word: touch nothing (nullptr: no check)
 };
 
 // The fused step (score + select + compact in one kernel) for units that
@@ -54,6 +60,10 @@ struct StepArgs {
   void* v;                // values
   int32_t* keep;          // [L][S][Hkv][budget]
   int32_t* free_blocks;   // paged FREE_BLOCKS output or nullptr
+  // With s.status set: reset_status = 1 clears the word (workgroup 0; no
+  // kernel before this launch in the call wrote it), else a nonzero word
+  // leaves everything untouched.
+  int32_t reset_status;
 };
 
 // Builds the device table of triggered sequences (Geom::dtab) from device
@@ -65,6 +75,20 @@ struct TableArgs {
   int32_t* free_counts;   // device [num_seqs] or nullptr
   int32_t num_seqs, budget, trigger, max_len;
   int32_t block_size;     // paged block size; 0 for the contiguous layout
+  uint32_t* status;       // the call's status word: cleared, then the check below
+  const int32_t* bt;      // paged block table to check, or nullptr (no check)
+  int32_t maxblk, nblk;   // its row length and the pool size
+};
+
+// First kernel of a call on host lengths: clears the status word (reset),
+// then checks the triggered sequences' block ids against the pool (bt
+// non-null) and sets kBadBlockId for an id outside [0, g.nblk).
+struct PrologueArgs {
+  Geom g;
+  TrigTable tt;
+  uint32_t* status;
+  const int32_t* bt;      // paged block table to check, or nullptr
+  int32_t reset;
 };
 
 // Redundancy through the explicit cosine Gram matrix (rkv_redundancy_gram).
@@ -90,6 +114,10 @@ struct WindowArgs {
 };
 
 hipError_t launch_window_store(const WindowArgs& a, hipStream_t st);
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
+// Bound of the key-span wait in s_memrealtime ticks (100 MHz), process-wide.
+void set_span_wait_ticks(int64_t ticks);
+int64_t span_wait_ticks();
 hipError_t launch_table(const TableArgs& a, hipStream_t st);
 int gram_block_rows(int max_len, int d);
 hipError_t launch_gram(const GramArgs& a, hipStream_t st);

@@ -16,10 +16,13 @@
 // on other streams can only delay some of them (it finishes and frees its
 // room); two such span launches at once on one device could hold each
 // other's room, which is why the interface asks for them on one stream.  The wait is a
-// spin on a per-unit counter (zeroed by a small kernel first), bounded at
-// one second so that no launch can hang the device; a launch that reached
-// the bound would finish with wrong scores -- it is never reached when the
-// launch's workgroups are dispatched.
+// spin on a per-unit counter (zeroed by a small kernel first), bounded (one
+// second unless the caller sets another bound) so that no launch can hang
+// the device; it is never reached when the launch's workgroups are
+// dispatched.  A span whose wait reaches the bound sets kSpanTimeout in the
+// call's status word and finishes with wrong scores; the selection and
+// compaction kernels of the call then leave the keep rows and the cache
+// untouched.
 #pragma once
 
 #include <algorithm>
@@ -30,8 +33,8 @@
 namespace rkv {
 
 struct LongArgs {
+  int64_t wait_ticks;   // bound on the wait for the other spans (s_memrealtime, 100 MHz)
   int32_t chunks;       // C: workgroups (key spans) per unit
-  int32_t wait_ticks;   // bound on the wait for the other spans (s_memrealtime, 100 MHz)
   int32_t unit0;        // first unit of this launch: workgroup w takes span w % C of unit0 + w / C
 };
 
@@ -48,16 +51,25 @@ static __global__ void long_zero_kernel(ScoreArgs a, int C, int units) {
 
 // Every thread's earlier global stores are published, then this workgroup
 // adds one to the unit's counter and waits until it reaches target (or the
-// time bound passes).  All threads call it.
-__device__ __forceinline__ void span_signal_wait(uint32_t* cnt, uint32_t target, int wait_ticks) {
+// time bound passes: then kSpanTimeout goes into the status word; a bound of
+// 0 gives up at once and always reports it).  All threads call it.
+__device__ __forceinline__ void span_signal_wait(uint32_t* cnt, uint32_t target, int64_t wait_ticks,
+                                                 uint32_t* status) {
   __syncthreads();   // every store of the workgroup performed
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
-           __builtin_amdgcn_s_memrealtime() - t_start < (uint64_t)wait_ticks)
-      __builtin_amdgcn_s_sleep(2);
+    bool done = false;
+    if (wait_ticks > 0) {
+      for (;;) {
+        done = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (done || __builtin_amdgcn_s_memrealtime() - t_start >= (uint64_t)wait_ticks) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!done && status != nullptr)
+      __hip_atomic_fetch_or(status, kSpanTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
@@ -109,6 +121,9 @@ __global__ __launch_bounds__(kUnitThreads) void score_long_kernel(ScoreArgs a, L
   const int C = la.chunks;
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
   const int c = blockIdx.x % C, t = threadIdx.x, gw = a.gw;
+  // a bad block id (set before this launch, so every span reads the same
+  // value): the pool must not be read
+  if (step_aborted(a.status, kBadBlockId)) return;
   {
     const int ui = la.unit0 + blockIdx.x / C;
     if (ui >= units) return;
@@ -121,7 +136,7 @@ __global__ __launch_bounds__(kUnitThreads) void score_long_kernel(ScoreArgs a, L
     // publish this span's record, wait for the unit's other spans, merge
     auto exchange = [&](bool empty) {
       publish_span_stats(L, recs, a.rec, c, gw, empty);
-      span_signal_wait(cnt, (uint32_t)C, la.wait_ticks);
+      span_signal_wait(cnt, (uint32_t)C, la.wait_ticks, a.status);
       if (!empty) merge_span_stats(L, recs, a.rec, C, gw);
     };
 
@@ -161,7 +176,7 @@ hipError_t launch_long_t(const ScoreArgs& a, int chunks, hipStream_t st) {
   hipLaunchKernelGGL(long_zero_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a, chunks, units);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int u0 = 0; u0 < units; u0 += per) {
-    LongArgs la{chunks, 100000000, u0};   // 1 s: far beyond any wait of a resident launch
+    LongArgs la{span_wait_ticks(), chunks, u0};   // default 1 s: far beyond any wait of a resident launch
     const int grid = std::min(per, units - u0) * chunks;
     hipLaunchKernelGGL((score_long_kernel<PAGED, D, RT>), dim3(grid), dim3(kUnitThreads), 0, st, a, la);
     if ((e = hipGetLastError()) != hipSuccess) return e;

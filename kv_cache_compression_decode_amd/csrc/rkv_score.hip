@@ -2,6 +2,8 @@
 // rkv_unit_impl.h for bf16 units that fit on chip, the key-span kernel of
 // rkv_long_impl.h for longer bf16 units, else the two kernels of
 // rkv_score_impl.h (one translation unit per cache dtype, head_dim, layout).
+#include <atomic>
+
 #include "rkv_step_impl.h"
 
 namespace rkv {
@@ -20,11 +22,16 @@ hipError_t dispatch_long_bf16_d128_contig(const ScoreArgs&, int, int, hipStream_
 hipError_t dispatch_long_bf16_d128_paged(const ScoreArgs&, int, int, hipStream_t);
 
 namespace {
+std::atomic<int64_t> g_span_wait_ticks{100000000};   // 1 s at 100 MHz
+
 int long_chunks(const ScoreArgs& a) {
   const int nmax = a.g.d == 64 ? UnitShape<64>::NMAX : UnitShape<128>::NMAX;
   return (a.max_len + nmax - 1) / nmax;
 }
 }  // namespace
+
+void set_span_wait_ticks(int64_t ticks) { g_span_wait_ticks.store(ticks, std::memory_order_relaxed); }
+int64_t span_wait_ticks() { return g_span_wait_ticks.load(std::memory_order_relaxed); }
 
 bool score_single_pass(const ScoreArgs& a, bool bf16, int max_len) {
   const int rt2 = (a.gw + 2 + 15) / 16;

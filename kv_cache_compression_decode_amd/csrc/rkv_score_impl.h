@@ -255,14 +255,11 @@ struct KeyRows {
   int shift, d;
   __device__ __forceinline__ void init(const Geom& g, const int32_t* table, const Unit& u) {
     d = g.d;
+    base = head_base(g, u.l, u.s, u.h);
     if constexpr (PAGED) {
-      const int bs = 1 << g.bs_shift;
       shift = g.bs_shift;
-      blk_stride = (int64_t)g.hkv * bs * g.d;
-      base = ((int64_t)u.l * g.nblk * g.hkv + u.h) * bs * g.d;
+      blk_stride = ((int64_t)g.hkv << g.bs_shift) * g.d;
       bt = table + (int64_t)u.s * g.maxblk;
-    } else {
-      base = (((int64_t)u.l * g.num_seqs + u.s) * g.hkv + u.h) * g.cap * g.d;
     }
   }
   __device__ __forceinline__ int64_t at(int t) const {
@@ -465,6 +462,7 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(ScoreArgs a) {
   const Unit u = decode_unit(a.g, a.tt, unit_id);
   const int key_base = chunk * kChunk;
   if (key_base >= u.n) return;
+  if (step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
 
   __shared__ float red_m[4][RT * 16], red_z[4][RT * 16], red_s[4][D];
   __shared__ float q_lds[BF16 ? 1 : RT * 16 * D];
@@ -496,6 +494,7 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(ScoreArgs a) {
   const Unit u = decode_unit(a.g, a.tt, unit_id);
   const int key_base = chunk * kChunk;
   if (key_base >= u.n) return;
+  if (step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
 
   __shared__ float row_m[RT * 16], row_iz[RT * 16], s_lds[D];
   __shared__ uint16_t s_bf[2][BF16 ? D : 1];

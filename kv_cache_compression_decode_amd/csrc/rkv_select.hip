@@ -17,6 +17,7 @@ __global__ __launch_bounds__(T) void select_kernel(SelectArgs a) {
   const int heads = a.g.shared ? a.g.hkv : 1;   // score rows ranked together
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x * heads);   // head 0 when shared
   if (u.n == 0) return;   // past the device table's count
+  if (step_aborted(a.status)) return;   // the step failed a device check: keep rows untouched
   const int cand = u.n - a.g.window;
   const int want = a.g.budget - a.g.window;
   const float* srow = a.scores + out_row(a.g, u) * a.score_stride;

@@ -66,6 +66,11 @@ __global__ __launch_bounds__(kUnitThreads) void step_unit_kernel(StepArgs sa) {
 
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
   if (u.n == 0) return;   // past the device table's count
+  if (sa.reset_status) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0u;   // nothing else of the call writes it
+  } else if (step_aborted(a.status)) {
+    return;   // the step failed a device check: leave everything untouched
+  }
   const int n = u.n, budget = a.g.budget, window = a.g.window;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, g4 = lane >> 4;

@@ -38,11 +38,20 @@ class RKVStep:
                     self.importance, self.redundancy, self.workspace, self.ws_bytes, stream)
 
     def select(self, seq_lens, stream=None) -> None:
-        B.rkv_select(self.cfg, self.num_seqs, seq_lens, self.scores, self.max_len, self.keep, stream)
+        B.rkv_select(self.cfg, self.num_seqs, seq_lens, self.scores, self.max_len, self.keep,
+                     self.workspace, self.ws_bytes, stream)
 
     def compact(self, cache: B.rkv_cache, seq_lens: np.ndarray, stream=None) -> None:
         B.rkv_compact(self.cfg, cache, self.num_seqs, seq_lens, self.keep, self.free_blocks,
-                      self.free_capacity, self.free_counts, stream)
+                      self.free_capacity, self.free_counts, self.workspace, self.ws_bytes, stream)
+
+    def status(self, stream=None) -> int:
+        """Flags of the last step's device checks (0: none failed); waits for the stream."""
+        return B.rkv_device_status(self.workspace, stream)
+
+    def device_status(self, stream=None) -> int:
+        """Flags of the last rkv_step_device call's device checks."""
+        return B.rkv_device_status(self.dev_ws, stream)
 
     def __call__(self, cache: B.rkv_cache, q_window, seq_lens: np.ndarray, stream=None) -> None:
         """score, select, compact as three calls; seq_lens (int32 numpy) is updated in place."""

@@ -38,15 +38,41 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define RKV_MAX_WINDOW_ROWS (\d+)", text).group(1)) == B.RKV_MAX_WINDOW_ROWS
 
 
-def test_struct_layouts():
-    assert ctypes.sizeof(B.rkv_config) == 48
-    assert ctypes.sizeof(B.rkv_cache) == 40
-    assert B.rkv_cache.block_table.offset == 24
+def test_header_flag_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("RKV_DEVICE_SPAN_TIMEOUT", "RKV_DEVICE_BAD_BLOCK_ID"):
+        assert int(re.search(rf"#define {name} (\d+)u", text).group(1)) == getattr(B, name)
+    assert int(re.search(r"RKV_ERR_DEVICE_CHECK = (\d+)", text).group(1)) == B.RKV_ERR_DEVICE_CHECK
+
+
+def test_struct_layouts(tmp_path):
+    """The ctypes structures have the sizes and field offsets a C compiler
+    gives the header's structures (gcc, host only)."""
+    import subprocess
+    fields = {"rkv_config": [f[0] for f in B.rkv_config._fields_],
+              "rkv_cache": [f[0] for f in B.rkv_cache._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rkv.h"', 'int main(void) {']
+    for st, names in fields.items():
+        lines.append(f'  printf("{st} size %zu\\n", sizeof({st}));')
+        for f in names:
+            lines.append(f'  printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for st, cls in (("rkv_config", B.rkv_config), ("rkv_cache", B.rkv_cache)):
+        assert got[(st, "size")] == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert got[(st, f)] == getattr(cls, f).offset, (st, f)
 
 
 def test_status_strings():
     for s, name in [(0, "RKV_OK"), (1, "RKV_ERR_INVALID_ARG"), (2, "RKV_ERR_UNSUPPORTED"),
-                    (3, "RKV_ERR_WORKSPACE"), (4, "RKV_ERR_HIP")]:
+                    (3, "RKV_ERR_WORKSPACE"), (4, "RKV_ERR_HIP"), (5, "RKV_ERR_DEVICE_CHECK")]:
         assert B.rkv_status_string(s) == name
 
 
@@ -67,7 +93,7 @@ FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
 def cache(**kw):
     return B.make_cache(kw.get("k", FAKE), kw.get("v", FAKE), kw.get("capacity", 2048),
                         kw.get("num_blocks", 0), kw.get("block_table", None),
-                        kw.get("max_blocks", 0))
+                        kw.get("max_blocks", 0), kw.get("layer_stride", 0))
 
 
 def test_trigger_rule():
@@ -79,9 +105,10 @@ def test_trigger_rule():
 
 def test_workspace_size_formula():
     c = cfg()
-    # one record of 2*G*w + d floats per (unit, 256-key chunk), 256-byte rounded
+    # the 256-byte status block, then one record of 2*G*w + d floats per
+    # (unit, 256-key chunk), 256-byte rounded
     n = B.rkv_workspace_size(c, 1, 1152)
-    assert n == 1 * 32 * 8 * math.ceil(1152 / 256) * (2 * 4 * 8 + 128) * 4
+    assert n == 256 + 1 * 32 * 8 * math.ceil(1152 / 256) * (2 * 4 * 8 + 128) * 4
     assert B.rkv_workspace_size(c, 200, 1152) == B.rkv_workspace_size(c, 128, 1152)
     assert B.rkv_workspace_size(cfg(head_dim=96), 1, 1152) == 0
 
@@ -167,6 +194,68 @@ def test_nothing_triggered_is_a_no_op():
     B.rkv_score(c, cache(), None, 0, None, None, 0, None, None, None, 0, None)
 
 
+def test_layer_stride_checked():
+    """layer_stride: 0 (packed), or at least one packed layer and a multiple of
+    16 bytes."""
+    c = cfg()
+    packed = 1 * 8 * 2048 * 128                      # S * Hkv * capacity * d
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=cache(layer_stride=-8))
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=cache(layer_stride=packed + 4))   # 8 bytes
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=cache(layer_stride=packed - 8))
+    expect(B.RKV_ERR_INVALID_ARG, gram, c, ca=cache(layer_stride=packed - 8))
+    lens = np.array([1152], np.int32)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_compact, c, cache(layer_stride=packed - 8), 1, lens, FAKE)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_step, c, cache(layer_stride=7), FAKE, 1, lens, FAKE, 1152,
+           FAKE)
+    fc = cfg(dtype="f32")
+    expect(B.RKV_ERR_INVALID_ARG, score, fc, ca=cache(layer_stride=packed + 2))  # 8 bytes
+    pc = cfg(layout="paged")
+    ppacked = 100 * 8 * 16 * 128                     # num_blocks * Hkv * block_size * d
+    expect(B.RKV_ERR_INVALID_ARG, score, pc, ca=cache(num_blocks=100, block_table=FAKE,
+                                                       max_blocks=72, layer_stride=ppacked - 8))
+    assert lens[0] == 1152
+
+
+def test_check_block_table_flag():
+    c = cfg(layout="paged")
+    c.check_block_table = 2
+    pca = cache(num_blocks=100, block_table=FAKE, max_blocks=72)
+    expect(B.RKV_ERR_INVALID_ARG, score, c, ca=pca)
+    c.check_block_table = 1
+    lens = np.array([1152], np.int32)
+    # the device check needs a workspace for its status word
+    expect(B.RKV_ERR_WORKSPACE, B.rkv_step, c, pca, FAKE, 1, lens, FAKE, 1152, FAKE, FAKE, 8)
+    expect(B.RKV_ERR_WORKSPACE, B.rkv_compact, c, pca, 1, lens, FAKE, FAKE, 8)
+    assert lens[0] == 1152
+    assert B.make_config(1, 4, 1, 64, 128, 32, 8, 0.1, layout="paged",
+                         check_block_table=True).check_block_table == 1
+
+
+def test_status_workspace_checked():
+    """rkv_select and rkv_compact accept no workspace, or a 256-byte aligned
+    one of at least 256 bytes; the status query needs one."""
+    c = cfg()
+    lens = np.array([1152], np.int32)
+    expect(B.RKV_ERR_WORKSPACE, B.rkv_select, c, 1, lens, FAKE, 1152, FAKE, FAKE * 4 + 16, 4096)
+    expect(B.RKV_ERR_WORKSPACE, B.rkv_select, c, 1, lens, FAKE, 1152, FAKE, FAKE * 4, 128)
+    expect(B.RKV_ERR_WORKSPACE, B.rkv_compact, c, cache(), 1, lens, FAKE, None, 0, None,
+           FAKE * 4 + 16, 4096)
+    expect(B.RKV_ERR_INVALID_ARG, B.rkv_device_status, None)
+    assert lens[0] == 1152
+
+
+def test_span_wait_bound():
+    prev = B.rkv_set_span_wait_us(0)
+    try:
+        assert prev == 1000000
+        assert B.rkv_set_span_wait_us(-1) == -1
+        assert B.rkv_set_span_wait_us(60000001) == -1
+        assert B.rkv_set_span_wait_us(250) == 0
+        assert B.rkv_set_span_wait_us(prev) == 250
+    finally:
+        B.rkv_set_span_wait_us(1000000)
+
+
 def test_binding_requires_inplace_lengths():
     with pytest.raises(TypeError):
         B.rkv_compact(cfg(), cache(), 1, [1152], FAKE)
@@ -181,7 +270,7 @@ def step_dev(c, ca=None, n=1, lens=FAKE, max_len=1152, stride=1152, keep=FAKE, f
 def test_step_device_workspace_size():
     c = cfg()
     table = (1 + 3 * 4) * 4
-    table = (table + 255) // 256 * 256
+    table = 256 + (table + 255) // 256 * 256     # the status block, then the table
     # fused at this shape (bf16, N <= 1280, G*w = 32): only the table
     assert B.rkv_step_device_workspace_size(c, 4, 1152) == table
     # not fused (N > 1280): plus one record per (unit, 256-key chunk) for every sequence
