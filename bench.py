@@ -61,6 +61,9 @@ def parse():
                    help="time rkv_window_store (one decode step's queries, all layers, into the ring)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed region, one 256 MiB device copy (counter calibration)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the records measured after the timed region (the Gram on the matrix "
+                        "cores, the three calls kernel by kernel, the streaming peaks)")
     args = p.parse_args()
     if args.steps is not None and args.steps < 1:
         p.error("--steps must be >= 1")
@@ -106,15 +109,24 @@ def measured_traffic(kernel: str, workload: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(spec, case, seconds: float):
-    """The oracle, as it stands, on this host's cores: units of the same
-    workload until the time budget is spent; reported as steps/s."""
-    from oracle import rkv_oracle as O
+def cpu_threads() -> int:
+    """Threads the oracle can run on: its BLAS pool, bounded by the cores this
+    process may use (its CPU affinity)."""
+    usable = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        cores = 1
+        blas = 1
+    return max(1, min(usable, blas))
+
+
+def cpu_baseline(spec, case, seconds: float):
+    """The oracle, as it stands, on this host's cores: units of the same
+    workload, three samples of seconds / 3 each; the median sample's rate,
+    reported as steps/s."""
+    from oracle import rkv_oracle as O
+    cores = cpu_threads()
     units = [(s, l, h) for s in range(spec.num_seqs) for l in range(spec.num_layers)
              for h in range(spec.num_kv_heads)
              if case.lens0[s] >= spec.budget + spec.buffer]
@@ -128,12 +140,15 @@ def cpu_baseline(spec, case, seconds: float):
             done += 1
         return done, time.perf_counter() - t0
 
-    done, dt = sample(seconds)
-    steps_per_s = done / dt / len(units)
+    runs = sorted((done / dt, done, dt) for done, dt in (sample(seconds / 3) for _ in range(3)))
+    rate, done, dt = runs[1]
+    steps_per_s = rate / len(units)
     out = {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
-           "cpu": cpu_model(),
-           "sample": f"{done} of the step's {len(units)} units (float64 numpy, explicit N x N "
-                     f"Gram), {dt:.1f} s; value = units/s / units per step"}
+           "cpu": cpu_model(), "cores_usable": len(os.sched_getaffinity(0)),
+           "samples_steps_per_s": [round(r[0] / len(units), 4) for r in runs],
+           "sample": f"median of 3 samples of {seconds / 3:.1f} s: {done} of the step's "
+                     f"{len(units)} units in {dt:.1f} s (float64 numpy, explicit N x N Gram); "
+                     f"value = units/s / units per step"}
     try:   # the same oracle on one thread, a third of the time budget
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
@@ -146,6 +161,15 @@ def cpu_baseline(spec, case, seconds: float):
 
 
 def cpu_model() -> str:
+    """The CPU model name as lscpu gives it (else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
@@ -155,13 +179,62 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def measured_peaks(torch, stream) -> dict:
-    """Achievable peaks measured on this GPU, next to the spec figures: a
-    1 GiB device-to-device copy (read + write bytes / time) for HBM, and an
-    8192^3 bf16 matrix product through torch (the vendor GEMM library) for
-    the matrix cores.  Best of five timed repetitions each."""
+def stream_peaks(torch, stream) -> dict:
+    """HBM bandwidth of this repository's streaming kernels (librkv_membench.so:
+    16-byte accesses, each workgroup a contiguous stretch, eight loads in
+    flight per lane) on 2 GiB buffers, eight times the 256 MB last-level
+    cache: a read of every byte, and a copy (bytes read + bytes written).
+    Best over launch sizes of 4, 8 and 16 workgroups per compute unit and
+    five repetitions each."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_compression_decode_amd", "librkv_membench.so"))
+    lib.rkv_membench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    lib.rkv_membench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int32, ctypes.c_void_p]
     dev = torch.device("cuda:0")
+    nbytes = 2 << 30
+    a = torch.full((nbytes,), 7, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     out = {}
+    for name, moved in (("read", 1), ("copy", 2)):
+        best = None
+        for per_cu in (4, 8, 16):
+            for rep in range(6):
+                ev[0].record(stream)
+                if name == "read":
+                    rc = lib.rkv_membench_read(a.data_ptr(), nbytes, sink.data_ptr(), cus * per_cu,
+                                               stream.cuda_stream)
+                else:
+                    rc = lib.rkv_membench_copy(b.data_ptr(), a.data_ptr(), nbytes, cus * per_cu,
+                                               stream.cuda_stream)
+                ev[1].record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"rkv_membench_{name}: {rc}")
+                torch.cuda.synchronize()
+                if rep == 0:
+                    continue   # the first launch of a shape warms up
+                t = ev[0].elapsed_time(ev[1]) * 1e-3
+                if best is None or t < best[0]:
+                    best = (t, per_cu)
+        out[f"hbm_stream_{name}_GBps"] = round(moved * nbytes / best[0] / 1e9, 1)
+        out[f"hbm_stream_{name}_workgroups_per_cu"] = best[1]
+    del a, b
+    torch.cuda.synchronize()
+    return out
+
+
+def measured_peaks(torch, stream) -> dict:
+    """Achievable peaks measured on this GPU, next to the spec figures: the
+    streaming kernels above; a 1 GiB device-to-device copy by the runtime
+    (read + write bytes / time); and an 8192^3 bf16 matrix product through
+    torch (the vendor GEMM library) for the matrix cores.  Best of five timed
+    repetitions each."""
+    dev = torch.device("cuda:0")
+    out = stream_peaks(torch, stream)
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -370,9 +443,15 @@ def main():
         roofline["traffic"] = tb
     # (not in counter runs: the calibration copy must be the last copy they see)
     peaks = None if args.copy_probe else measured_peaks(torch, stream)
-    if peaks:
-        roofline["peak_measured"] = peaks["hbm_copy_GBps"]
-        roofline["frac_measured"] = round(achieved / peaks["hbm_copy_GBps"], 4)
+    if peaks:   # the copy rate of our own streaming kernel: the step both reads and writes
+        roofline["peak_measured"] = peaks["hbm_stream_copy_GBps"]
+        roofline["peak_measured_kind"] = "this repository's streaming copy kernel, 2 GiB buffers"
+        roofline["frac_measured"] = round(achieved / peaks["hbm_stream_copy_GBps"], 4)
+    extras = {}
+    if not (args.no_extras or args.copy_probe or args.three_calls or args.device_lens
+            or args.shared or restore):
+        extras["roofline_mfma"] = gram_record(spec, case, stream, peaks)
+        extras["three_calls"] = three_call_record(spec, case, step, copies, caches, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -414,9 +493,112 @@ def main():
                             "ms_per_step = mean per-step event interval" if restore else ""),
         "moved_rows": moved_rows,
         "measured_peaks": peaks,
+        **extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def gram_record(spec, case, stream, peaks, launches=50):
+    """The redundancy through the explicit cosine Gram (rkv_redundancy_gram) on
+    the same batch, against the dense bf16 matrix-core peak: 2 N^2 d flops per
+    unit (every product of the unit's full N x N Gram, no symmetry used) over
+    the kernel's mean launch time (HIP events around back-to-back launches;
+    the call only reads the cache)."""
+    import numpy as np
+    import torch
+
+    from gpu_harness import config_of
+    from kv_cache_compression_decode_amd import binding as B
+
+    lens0 = case.lens0.astype(np.int32)
+    maxn = int(lens0.max())
+    trig = lens0 >= spec.budget + spec.buffer
+    red = torch.empty((spec.num_layers * spec.num_seqs * spec.num_kv_heads, maxn),
+                      dtype=torch.float32, device="cuda")
+    cfg = config_of(spec)
+    for _ in range(3):
+        B.rkv_redundancy_gram(cfg, case.cache, spec.num_seqs, lens0, red, maxn, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(launches):
+        B.rkv_redundancy_gram(cfg, case.cache, spec.num_seqs, lens0, red, maxn, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / launches
+    flops = sum(2.0 * int(n) ** 2 * spec.head_dim for n in lens0[trig]) * spec.num_layers * spec.num_kv_heads
+    tflops = flops / (us * 1e-6) / 1e12
+    rec = {"bound": "mfma", "kernel": "gram", "entry": "rkv_redundancy_gram",
+           "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "us": round(us, 2),
+           "flops_per_launch": flops,
+           "work": "2 N^2 d flops per unit: every product of the full N x N Gram (no symmetry)",
+           "traffic": measured_traffic("gram", spec.name), "launches": launches}
+    if peaks:
+        rec["peak_measured"] = peaks["bf16_gemm_TFLOPs"]
+        rec["frac_measured"] = round(tflops / peaks["bf16_gemm_TFLOPs"], 4)
+    return rec
+
+
+def three_call_record(spec, case, step, copies, caches, stream, reps=10):
+    """The step as three calls (rkv_score, rkv_select, rkv_compact) on the same
+    batch, against 8 TB/s.  Each call is launched reps times back to back
+    between one pair of HIP events on its stream (so nothing runs between the
+    launches and interval / reps is the call's duration): scoring and
+    selection on one cache (they only read it), compaction on reps pristine
+    copies prepared beforehand.  Algorithmic bytes: scoring reads the keys
+    once (N d 2 B), the window queries, and writes the scores; selection reads
+    the scores and writes the keep lists; compaction reads and writes the
+    moved K and V rows and reads the keep lists (once per K and per V
+    workgroup)."""
+    import numpy as np
+    import torch
+
+    lens0 = case.lens0.astype(np.int32)
+    trig = lens0 >= spec.budget + spec.buffer
+    units = int(trig.sum()) * spec.num_layers * spec.num_kv_heads
+    esz = 2 if spec.dtype == "bf16" else 4
+    row = spec.head_dim * esz
+    tokens = int(sum(int(n) for n in lens0[trig])) * spec.num_layers * spec.num_kv_heads
+    reps = min(reps, len(caches))
+    for (kc, vc) in copies[:reps]:
+        kc.copy_(case.k)
+        vc.copy_(case.v)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    calls = {
+        "score": lambda i: step.score(caches[0], case.q, lens0.copy(), stream),
+        "select": lambda i: step.select(lens0.copy(), stream),
+        "compact": lambda i: step.compact(caches[i], lens0.copy(), stream),
+    }
+    for name in ("score", "select"):   # warm-up (compaction: its copies are single-use)
+        calls[name](0)
+    torch.cuda.synchronize()
+    for j, name in enumerate(("score", "select", "compact")):
+        ev[2 * j].record(stream)
+        for i in range(reps):
+            calls[name](i)
+        ev[2 * j + 1].record(stream)
+    torch.cuda.synchronize()
+    keep = step.keep.view(spec.num_layers, spec.num_seqs, spec.num_kv_heads, spec.budget)
+    keep = keep.cpu().numpy()[:, trig].reshape(-1, spec.budget)
+    moved = int((keep != np.arange(spec.budget)[None, :]).sum())
+    gw = spec.group * spec.window
+    nbytes = {"score": tokens * row + units * gw * row + tokens * 4,
+              "select": tokens * 4 + units * spec.budget * 4,
+              "compact": moved * row * 2 * 2 + units * spec.budget * 4 * 2}
+    kern = {}
+    for j, name in enumerate(("score", "select", "compact")):
+        us = ev[2 * j].elapsed_time(ev[2 * j + 1]) * 1e3 / reps
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        kern[name] = {"us": round(us, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "bound": "hbm" if name != "select" else "latency",
+                      "traffic": measured_traffic(name, spec.name)}
+    return {"entry": "rkv_score+rkv_select+rkv_compact", "reps": reps,
+            "ms_per_step": round(sum(k["us"] for k in kern.values()) / 1e3, 4),
+            "moved_rows": moved, "kernels": kern,
+            "kernel_timing": "per call, HIP events around reps back-to-back launches / reps"}
 
 
 def window_store_bench(args, spec):

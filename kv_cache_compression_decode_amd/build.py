@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librkv.so")
+# streaming bandwidth kernels the benchmark measures HBM with (not part of the step)
+MEMBENCH_SRC = os.path.join(PKG, "membench", "rkv_membench.hip")
+MEMBENCH_OUT = os.path.join(PKG, "librkv_membench.so")
 EXAMPLE = os.path.join(PKG, "rkv_c_example")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -61,6 +64,10 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined",
           "-Wl,-soname,librkv.so", *objs, "-o", tmp], verbose)
     os.replace(tmp, OUT)
+    tmp = MEMBENCH_OUT + ".tmp"
+    _run([HIPCC, *FLAGS, "-shared", "-Wl,--no-undefined", "-Wl,-soname,librkv_membench.so",
+          MEMBENCH_SRC, "-o", tmp], verbose)
+    os.replace(tmp, MEMBENCH_OUT)
     # a caller of the C ABI without Python (run by the GPU tests), linked against
     # the library next to it
     _run([HIPCC, *FLAGS, os.path.join(PKG, "examples", "rkv_c_example.cpp"), f"-L{PKG}", "-lrkv",

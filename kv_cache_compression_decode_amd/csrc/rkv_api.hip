@@ -296,7 +296,9 @@ hipError_t prologue(const rkv::Geom& g, const rkv::TrigTable& tt, void* ws, cons
 // most kMaxTrig sequences each; those that cannot run fused score, then
 // select, then compact -- scoring of all of them first, so that a device
 // check failing in any of them stops every write of the call -- and the
-// fused launches come last.
+// fused launches come last.  The status word is cleared by the call's first
+// kernel that touches it: the block-check prologue, else the first scoring
+// launch, else the first fused launch.
 rkv_status step_impl(const rkv_config* cfg, const rkv_cache* cache, const void* q_window,
                      int32_t num_seqs, int32_t* h_seq_lens, float* scores, int32_t score_stride,
                      int32_t* keep, int32_t* free_blocks, int32_t free_capacity,
@@ -351,15 +353,16 @@ rkv_status step_impl(const rkv_config* cfg, const rkv_cache* cache, const void* 
       if (e != hipSuccess) return hip_fail(e, "select kernel LDS limit");
     }
     hipError_t e;
-    const bool pro = workspace != nullptr && (any_unfused || check);
-    if (pro) {
+    if (check) {
       for (size_t i = 0; i < plan.size(); ++i) {
         fill_table(a.tt, trig, plan[i].first, plan[i].cnt, nullptr);
         a.g.num_trig = plan[i].cnt;
-        if ((e = prologue(a.g, a.tt, workspace, cache, i == 0, check, hs)) != hipSuccess)
+        if ((e = prologue(a.g, a.tt, workspace, cache, i == 0, true, hs)) != hipSuccess)
           return hip_fail(e, "prologue launch");
       }
     }
+    a.check_blocks = check ? 1 : 0;
+    bool reset_pending = workspace != nullptr && !check;
     auto set_launch = [&](const Launch& p) {
       fill_table(a.tt, trig, p.first, p.cnt, offs.data());
       a.g.num_trig = p.cnt;
@@ -369,8 +372,11 @@ rkv_status step_impl(const rkv_config* cfg, const rkv_cache* cache, const void* 
     for (const Launch& p : plan) {
       if (p.fused) continue;
       set_launch(p);
+      a.reset_status = reset_pending ? 1 : 0;
+      reset_pending = false;
       if ((e = rkv::launch_score(a, bf16, hs)) != hipSuccess) return hip_fail(e, "score launch");
     }
+    a.reset_status = 0;
     for (const Launch& p : plan) {
       if (p.fused) continue;
       set_launch(p);
@@ -398,15 +404,15 @@ rkv_status step_impl(const rkv_config* cfg, const rkv_cache* cache, const void* 
       ca.status = a.status;
       if ((e = rkv::launch_compact(ca, hs)) != hipSuccess) return hip_fail(e, "compact launch");
     }
-    // fused launches: after a prologue they check the status word; without
-    // one the first of them clears it
-    bool reset_pending = workspace != nullptr && !pro;
+    // fused launches: after a kernel of the call touched the status word
+    // they check it; else the first of them clears it
+    const bool touched = check || any_unfused;
     for (const Launch& p : plan) {
       if (!p.fused) continue;
       set_launch(p);
       rkv::StepArgs sa{};
       sa.s = a;
-      sa.s.status = pro || reset_pending ? status_of(workspace) : nullptr;
+      sa.s.status = touched || reset_pending ? status_of(workspace) : nullptr;
       sa.reset_status = reset_pending ? 1 : 0;
       reset_pending = false;
       sa.k = cache->k;
@@ -478,14 +484,19 @@ rkv_status rkv_score(const rkv_config* cfg, const rkv_cache* cache, const void* 
                                      importance, redundancy, workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool check = checks_blocks(cfg);
+  a.check_blocks = check ? 1 : 0;
   for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
     const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
     fill_table(a.tt, trig, first, cnt, nullptr);
     a.g.num_trig = cnt;
     a.max_len = max_len_of(trig, first, cnt);
     a.max_chunks = (a.max_len + rkv::kChunk - 1) / rkv::kChunk;
-    hipError_t e = prologue(a.g, a.tt, workspace, cache, first == 0, check, hs);
-    if (e != hipSuccess) return hip_fail(e, "prologue launch");
+    hipError_t e;
+    // the status word: cleared (and the block ids checked) by a prologue when
+    // checking, else cleared by the first scoring launch itself
+    if (check && (e = prologue(a.g, a.tt, workspace, cache, first == 0, true, hs)) != hipSuccess)
+      return hip_fail(e, "prologue launch");
+    a.reset_status = !check && first == 0 ? 1 : 0;
     e = rkv::launch_score(a, cfg->dtype == RKV_DTYPE_BF16, hs);
     if (e != hipSuccess) return hip_fail(e, "score launch");
   }
@@ -736,6 +747,7 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(dtab) + dev_table_bytes(num_seqs));
   a.g.num_trig = num_seqs;
   a.g.dtab = dtab;
+  a.check_blocks = checks_blocks(cfg) ? 1 : 0;   // the table kernel cleared and checked it
   a.max_len = max_len;
   a.max_chunks = (max_len + rkv::kChunk - 1) / rkv::kChunk;
   if (rkv::step_fusable(a, bf16)) {

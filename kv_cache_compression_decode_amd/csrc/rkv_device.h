@@ -77,12 +77,18 @@ constexpr uint32_t kSpanTimeout = RKV_DEVICE_SPAN_TIMEOUT;
 constexpr uint32_t kBadBlockId = RKV_DEVICE_BAD_BLOCK_ID;
 
 // True if a kernel of the step must leave everything untouched: the status
-// word (when the call has one) holds one of the flags in mask.  The word is
-// written only by kernels that run before the reader on the same stream, or
-// -- the span-timeout flag -- by key-span launches, which therefore test
-// only kBadBlockId.
+// word (when the call has one) holds one of the flags in mask.  Readers run
+// after every kernel of the call that clears or checks the word (on the same
+// stream); key-span launches, which set kSpanTimeout themselves, test only
+// kBadBlockId.
 __device__ __forceinline__ bool step_aborted(const uint32_t* status, uint32_t mask = ~0u) {
   return status != nullptr && (*status & mask) != 0u;
+}
+
+// Workgroup 0's first thread clears the status word (a launch that is the
+// first of its call to touch it).
+__device__ __forceinline__ void clear_status_first(uint32_t* status) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && status != nullptr) *status = 0u;
 }
 
 // Element offset of (layer l, kv head h)'s row 0 in a contiguous cache

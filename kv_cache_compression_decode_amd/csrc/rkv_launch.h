@@ -25,10 +25,15 @@ struct ScoreArgs {
   int32_t rec;            // floats per chunk record: 2 * gw + d
   float lambda;
   float c;                // log2(e) / sqrt(d): raw dot -> log2-scaled logit
-  // Status word of the call's workspace, or nullptr.  Scoring kernels return
-  // at once if it holds kBadBlockId (the pool must not be read); key-span
-  // launches set kSpanTimeout in it.
+  // Status word of the call's workspace, or nullptr.  Key-span launches set
+  // kSpanTimeout in it.  check_blocks: a prologue checked the block ids, and
+  // scoring kernels return at once if it holds kBadBlockId (the pool must not
+  // be read).  reset_status: this launch clears it first (the call has no
+  // prologue; no earlier kernel of the call wrote it): the key-span counter
+  // kernel, the single-pass kernel or the stats kernel, from workgroup 0.
   uint32_t* status;
+  int32_t check_blocks;
+  int32_t reset_status;
 };
 
 struct SelectArgs {

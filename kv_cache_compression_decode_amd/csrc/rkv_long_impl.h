@@ -47,6 +47,7 @@ __device__ __forceinline__ uint32_t* long_counter(const ScoreArgs& a, int ui, in
 static __global__ void long_zero_kernel(ScoreArgs a, int C, int units) {
   const int ui = blockIdx.x * blockDim.x + threadIdx.x;
   if (ui < units) *long_counter(a, ui, C) = 0u;
+  if (a.reset_status) clear_status_first(a.status);
 }
 
 // Every thread's earlier global stores are published, then this workgroup
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kUnitThreads) void score_long_kernel(ScoreArgs a, L
   const int c = blockIdx.x % C, t = threadIdx.x, gw = a.gw;
   // a bad block id (set before this launch, so every span reads the same
   // value): the pool must not be read
-  if (step_aborted(a.status, kBadBlockId)) return;
+  if (a.check_blocks && step_aborted(a.status, kBadBlockId)) return;
   {
     const int ui = la.unit0 + blockIdx.x / C;
     if (ui >= units) return;

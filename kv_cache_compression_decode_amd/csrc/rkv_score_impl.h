@@ -462,7 +462,8 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(ScoreArgs a) {
   const Unit u = decode_unit(a.g, a.tt, unit_id);
   const int key_base = chunk * kChunk;
   if (key_base >= u.n) return;
-  if (step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
+  if (a.reset_status) clear_status_first(a.status);
+  if (a.check_blocks && step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
 
   __shared__ float red_m[4][RT * 16], red_z[4][RT * 16], red_s[4][D];
   __shared__ float q_lds[BF16 ? 1 : RT * 16 * D];
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(ScoreArgs a) {
   const Unit u = decode_unit(a.g, a.tt, unit_id);
   const int key_base = chunk * kChunk;
   if (key_base >= u.n) return;
-  if (step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
+  if (a.check_blocks && step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
 
   __shared__ float row_m[RT * 16], row_iz[RT * 16], s_lds[D];
   __shared__ uint16_t s_bf[2][BF16 ? D : 1];

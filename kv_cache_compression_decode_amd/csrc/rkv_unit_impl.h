@@ -363,7 +363,8 @@ __global__ __launch_bounds__(kUnitThreads) void score_unit_kernel(ScoreArgs a) {
   KeyFrag<true, D> kf[UnitShape<D>::NBW];
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
   if (u.n == 0) return;   // past the device table's count
-  if (step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
+  if (a.reset_status) clear_status_first(a.status);
+  if (a.check_blocks && step_aborted(a.status, kBadBlockId)) return;   // the pool must not be read
   unit_score<PAGED, D, RT>(a, u, L, kf, [](int) {}, [](int, float) {});
 }
 

@@ -341,3 +341,25 @@ def test_window_store_argument_errors():
     expect(B.RKV_ERR_UNSUPPORTED, wstore, cfg(head_dim=96))
     wstore(c, n=0, q=None, steps=None, ring=None)                     # nothing to store
     wstore(c, count=0, q=None, steps=None, ring=None)
+
+
+def test_membench_library_exports_its_header():
+    """The measurement-only streaming kernels: librkv_membench.so exports what
+    include/rkv_membench.h declares and rejects bad arguments before any launch."""
+    path = os.path.join(ROOT, "kv_cache_compression_decode_amd", "librkv_membench.so")
+    lib = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "rkv_membench.h")).read(),
+                  flags=re.S)
+    declared = sorted(set(re.findall(r"\b(rkv_[a-z_]+)\s*\(", text)))
+    assert declared == ["rkv_membench_copy", "rkv_membench_read"]
+    for name in declared:
+        assert hasattr(lib, name)
+    lib.rkv_membench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    lib.rkv_membench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    assert lib.rkv_membench_read(None, 16, FAKE, 0, None) == -1
+    assert lib.rkv_membench_read(FAKE + 4, 16, FAKE, 0, None) == -1
+    assert lib.rkv_membench_read(FAKE, 17, FAKE, 0, None) == -1
+    assert lib.rkv_membench_copy(FAKE, FAKE, 8, 0, None) == -1
+    assert lib.rkv_membench_copy(FAKE, FAKE, 0, 0, None) == 0       # nothing to do

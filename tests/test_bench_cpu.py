@@ -84,3 +84,12 @@ def test_bad_step_counts_are_rejected(argv):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "must be" in r.stderr
+
+
+def test_cpu_baseline_host_facts():
+    """The CPU baseline names the host's CPU model and counts the threads the
+    oracle may use (its BLAS pool within this process's CPU affinity)."""
+    b = load_bench()
+    assert 1 <= b.cpu_threads() <= len(os.sched_getaffinity(0))
+    model = b.cpu_model()
+    assert model and model != "unknown"
