@@ -337,13 +337,34 @@ rkv_status rkv_step_device(const rkv_config *cfg, const rkv_cache *cache, const 
                            int32_t *free_blocks, int32_t free_capacity, int32_t *d_free_counts,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* rkv_step without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments as rkv_step minus the workspace, same
+ * results bit for bit.  The scratch the step needs (the status word and the
+ * scoring records of launches that cannot run fused) lives in a 32 MiB
+ * device array of the library, one per GPU, held from the first call on that
+ * GPU until the process ends; the call allocates nothing.  Calls that
+ * overlap on one GPU (other streams, other host threads) share that array
+ * and race: keep them on one stream.  Its status word is read with
+ * rkv_device_status(NULL, ...).
+ * Errors: those of rkv_step; RKV_ERR_WORKSPACE when a launch that cannot run
+ * fused needs more than the 32 MiB (rkv_workspace_size for at most 128
+ * triggered sequences of the longest length, e.g. 8 sequences of 4352 keys
+ * of the paged Llama-8B workload take 25.5 MiB). */
+rkv_status rkv_step_noalloc(const rkv_config *cfg, const rkv_cache *cache, const void *q_window,
+                            int32_t num_seqs, int32_t *h_seq_lens,
+                            float *scores, int32_t score_stride, int32_t *keep,
+                            int32_t *free_blocks, int32_t free_capacity, int32_t *h_free_counts,
+                            void *stream);
+
 /* The status word of a workspace (its first 32-bit word) after the calls
  * enqueued on `stream` so far: waits for the stream, then copies the word to
  * the host (so it cannot be captured in a graph).  *flags (may be NULL)
  * receives it: RKV_DEVICE_SPAN_TIMEOUT, RKV_DEVICE_BAD_BLOCK_ID or 0.
  * Returns RKV_OK for 0, RKV_ERR_DEVICE_CHECK otherwise (the step left the
- * cache as it was; see rkv_compact for the lengths).
- * Errors: RKV_ERR_INVALID_ARG (workspace NULL), RKV_ERR_HIP. */
+ * cache as it was; see rkv_compact for the lengths).  workspace NULL: the
+ * word of rkv_step_noalloc's scratch on the current device.
+ * Errors: RKV_ERR_HIP. */
 rkv_status rkv_device_status(const void *workspace, void *stream, uint32_t *flags);
 
 /* Bound of the key-span wait, in microseconds, for launches enqueued after

@@ -39,7 +39,7 @@ EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_works
            "rkv_redundancy_gram", "rkv_window_store",
            "rkv_score", "rkv_select", "rkv_compact", "rkv_step",
            "rkv_step_device_workspace_size", "rkv_step_device", "rkv_device_status",
-           "rkv_set_span_wait_us")
+           "rkv_set_span_wait_us", "rkv_step_noalloc")
 
 
 class rkv_config(ctypes.Structure):
@@ -110,6 +110,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                     c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                     c_void_p, c_void_p, c_size_t, c_void_p]
     lib.rkv_step_device.restype = c_int32
+    lib.rkv_step_noalloc.argtypes = [P(rkv_config), P(rkv_cache), c_void_p, c_int32, P(c_int32),
+                                     c_void_p, c_int32, c_void_p, c_void_p, c_int32, P(c_int32),
+                                     c_void_p]
+    lib.rkv_step_noalloc.restype = c_int32
     lib.rkv_device_status.argtypes = [c_void_p, c_void_p, P(ctypes.c_uint32)]
     lib.rkv_device_status.restype = c_int32
     lib.rkv_set_span_wait_us.argtypes = [ctypes.c_int64]
@@ -258,9 +262,26 @@ def rkv_step_device(cfg, cache, q_window, num_seqs, d_seq_lens, max_len, scores,
                                   _stream(stream)))
 
 
+def rkv_step_noalloc(cfg, cache, q_window, num_seqs, seq_lens: np.ndarray, scores, score_stride,
+                     keep, free_blocks=None, free_capacity=0,
+                     free_counts: Optional[np.ndarray] = None, stream=None) -> None:
+    """rkv_step with the library's own scratch instead of a workspace."""
+    if not (isinstance(seq_lens, np.ndarray) and seq_lens.dtype == np.int32
+            and seq_lens.flags.c_contiguous):
+        raise TypeError("seq_lens must be a C-contiguous int32 numpy array (updated in place)")
+    if free_counts is not None and not (free_counts.dtype == np.int32
+                                        and free_counts.flags.c_contiguous):
+        raise TypeError("free_counts must be a C-contiguous int32 numpy array")
+    _check(load().rkv_step_noalloc(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q_window),
+                                   num_seqs, _i32p(seq_lens), _ptr(scores), score_stride,
+                                   _ptr(keep), _ptr(free_blocks), free_capacity,
+                                   _i32p(free_counts), _stream(stream)))
+
+
 def rkv_device_status(workspace, stream=None) -> int:
     """The workspace's status word (waits for the stream): 0, or the
-    RKV_DEVICE_* flags of the checks that failed.  Other errors raise."""
+    RKV_DEVICE_* flags of the checks that failed.  workspace None: the
+    scratch of rkv_step_noalloc on the current device.  Other errors raise."""
     flags = ctypes.c_uint32(0)
     st = load().rkv_device_status(_ptr(workspace), _stream(stream), ctypes.byref(flags))
     if st not in (RKV_OK, RKV_ERR_DEVICE_CHECK):

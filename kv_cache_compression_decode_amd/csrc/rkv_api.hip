@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -428,6 +429,41 @@ rkv_status step_impl(const rkv_config* cfg, const rkv_cache* cache, const void* 
   return RKV_OK;
 }
 
+// Scratch of the allocation-free entry point: the workspace rkv_step would
+// take, in a device array of the library's own (each GPU holds its copy at
+// its own address until the process ends).  Host code never passes the
+// array's name to a kernel or a copy: only the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+rkv_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RKV_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned256(p)) return fail(RKV_ERR_HIP, "scratch has no usable address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -785,9 +821,31 @@ rkv_status rkv_step_device(const rkv_config* cfg, const rkv_cache* cache, const 
   return RKV_OK;
 }
 
+rkv_status rkv_step_noalloc(const rkv_config* cfg, const rkv_cache* cache, const void* q_window,
+                            int32_t num_seqs, int32_t* h_seq_lens, float* scores,
+                            int32_t score_stride, int32_t* keep, int32_t* free_blocks,
+                            int32_t free_capacity, int32_t* h_free_counts, void* stream) {
+  g_err.clear();
+  void* ws = nullptr;
+  rkv_status st = scratch_address(&ws);
+  if (st != RKV_OK) return st;
+  st = step_impl(cfg, cache, q_window, num_seqs, h_seq_lens, scores, score_stride, keep,
+                 free_blocks, free_capacity, h_free_counts, ws, kScratchBytes,
+                 static_cast<hipStream_t>(stream));
+  if (st == RKV_ERR_WORKSPACE)
+    return fail(RKV_ERR_WORKSPACE, "the step needs more scratch than the %zu bytes rkv_step_noalloc holds (%s)",
+                kScratchBytes, g_err.c_str());
+  return st;
+}
+
 rkv_status rkv_device_status(const void* workspace, void* stream, uint32_t* flags) {
   g_err.clear();
-  if (workspace == nullptr) return fail(RKV_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace == nullptr) {   // the allocation-free entry's scratch
+    void* ws = nullptr;
+    const rkv_status st = scratch_address(&ws);
+    if (st != RKV_OK) return st;
+    workspace = ws;
+  }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   uint32_t word = 0;
   hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, hs);

@@ -240,7 +240,6 @@ def test_status_workspace_checked():
     expect(B.RKV_ERR_WORKSPACE, B.rkv_select, c, 1, lens, FAKE, 1152, FAKE, FAKE * 4, 128)
     expect(B.RKV_ERR_WORKSPACE, B.rkv_compact, c, cache(), 1, lens, FAKE, None, 0, None,
            FAKE * 4 + 16, 4096)
-    expect(B.RKV_ERR_INVALID_ARG, B.rkv_device_status, None)
     assert lens[0] == 1152
 
 
