@@ -30,11 +30,12 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "step": ["rkv_step_impl.h", "rkv_unit_impl.h", "rkv_select_impl.h", "rkv_score_impl.h",
-             "rkv_device.h"],
-    "compact": ["rkv_compact.hip", "rkv_device.h"],
-    "score": ["rkv_score_impl.h", "rkv_device.h"],
-    "select": ["rkv_select.hip", "rkv_device.h"],
-    "gram": ["rkv_gram.hip", "rkv_score_impl.h", "rkv_device.h"],
+             "rkv_device.h", "rkv_launch.h"],
+    "compact": ["rkv_compact.hip", "rkv_device.h", "rkv_launch.h"],
+    "score": ["rkv_unit_impl.h", "rkv_long_impl.h", "rkv_score_impl.h", "rkv_device.h",
+              "rkv_launch.h"],
+    "select": ["rkv_select.hip", "rkv_select_impl.h", "rkv_device.h", "rkv_launch.h"],
+    "gram": ["rkv_gram.hip", "rkv_score_impl.h", "rkv_device.h", "rkv_launch.h"],
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
 
@@ -547,7 +548,8 @@ def three_call_record(spec, case, step, copies, caches, stream, reps=10):
     between one pair of HIP events on its stream (so nothing runs between the
     launches and interval / reps is the call's duration): scoring and
     selection on one cache (they only read it), compaction on reps pristine
-    copies prepared beforehand.  Algorithmic bytes: scoring reads the keys
+    copies prepared beforehand (one more, before the timed launches, takes
+    the first launch, which also loads the kernel).  Algorithmic bytes: scoring reads the keys
     once (N d 2 B), the window queries, and writes the scores; selection reads
     the scores and writes the keep lists; compaction reads and writes the
     moved K and V rows and reads the keep lists (once per K and per V
@@ -561,18 +563,19 @@ def three_call_record(spec, case, step, copies, caches, stream, reps=10):
     esz = 2 if spec.dtype == "bf16" else 4
     row = spec.head_dim * esz
     tokens = int(sum(int(n) for n in lens0[trig])) * spec.num_layers * spec.num_kv_heads
-    reps = min(reps, len(caches))
-    for (kc, vc) in copies[:reps]:
+    reps = min(reps, len(caches) - 1)
+    for (kc, vc) in copies[:reps + 1]:
         kc.copy_(case.k)
         vc.copy_(case.v)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     calls = {
         "score": lambda i: step.score(caches[0], case.q, lens0.copy(), stream),
         "select": lambda i: step.select(lens0.copy(), stream),
-        "compact": lambda i: step.compact(caches[i], lens0.copy(), stream),
+        "compact": lambda i: step.compact(caches[i + 1], lens0.copy(), stream),
     }
-    for name in ("score", "select"):   # warm-up (compaction: its copies are single-use)
+    for name in ("score", "select"):   # warm-up: the first launch of a kernel loads it
         calls[name](0)
+    step.compact(caches[0], lens0.copy(), stream)   # copy 0 is the compaction's warm-up
     torch.cuda.synchronize()
     for j, name in enumerate(("score", "select", "compact")):
         ev[2 * j].record(stream)
