@@ -117,3 +117,35 @@ def unit(q_rows, keys, lam, budget, window):
     red = redundancy(keys)
     s = mixed(imp, red, lam)
     return imp, red, s, select_keep(s, len(keys), budget, window)
+
+
+# ------------------------------------------------------------- KARA-style window step
+
+def kara_scores(q_rows: Sequence[Row], keys: Sequence[Row]) -> List[float]:
+    """Every row's softmax over all window keys (no mask), averaged over rows:
+    the same loops as importance(), over the window's keys only."""
+    return importance(q_rows, keys)
+
+
+def kara_keep(scores: Sequence[float], keep: int, anchors: int, radius: int) -> List[int]:
+    """Token2Chunk by counting: rank_j = how many positions beat j (higher
+    score, or equal score at a lower position); anchors are the ranks below
+    `anchors`; a position is in a chunk if an anchor lies within radius; the
+    rest are taken in rank order among the positions outside every chunk."""
+    w = len(scores)
+
+    def beats(i, j):
+        return scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
+
+    rank = [sum(1 for i in range(w) if beats(i, j)) for j in range(w)]
+    in_chunk = [any(rank[a] < anchors and abs(a - j) <= radius for a in range(w)) for j in range(w)]
+    left = keep - sum(in_chunk)
+    out = []
+    for j in range(w):
+        if in_chunk[j]:
+            out.append(j)
+            continue
+        better = sum(1 for i in range(w) if not in_chunk[i] and beats(i, j))
+        if better < left:
+            out.append(j)
+    return out
