@@ -36,6 +36,8 @@ KERNEL_SOURCES = {
               "rkv_launch.h"],
     "select": ["rkv_select.hip", "rkv_select_impl.h", "rkv_device.h", "rkv_launch.h"],
     "gram": ["rkv_gram.hip", "rkv_score_impl.h", "rkv_device.h", "rkv_launch.h"],
+    "kara": ["rkv_kara.hip", "rkv_kara.h", "rkv_score_impl.h", "rkv_select_impl.h", "rkv_device.h",
+             "rkv_launch.h"],
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
 
@@ -58,6 +60,9 @@ def parse():
                    help="head-shared selection (one keep set per sequence and layer; three kernels)")
     p.add_argument("--gram", action="store_true",
                    help="time rkv_redundancy_gram (the explicit cosine Gram on the matrix cores) instead")
+    p.add_argument("--kara", action="store_true",
+                   help="time rkv_kara_step, the KARA-style window step (window 128 -> keep 32, "
+                        "4 anchors of radius 2), on the workload's shape")
     p.add_argument("--window-store", action="store_true",
                    help="time rkv_window_store (one decode step's queries, all layers, into the ring)")
     p.add_argument("--copy-probe", action="store_true",
@@ -291,6 +296,8 @@ def main():
     case = PagedCase(spec) if spec.layout == "paged" else ContigCase(spec)
     if args.gram:
         return gram_bench(args, spec, case)
+    if args.kara:
+        return kara_bench(args, spec, case)
     cfg = config_of(spec, shared=args.shared)
     copy_bytes = case.k.numel() * case.k.element_size() * 2
     # Paged pools too large to copy once per step (the 8-sequence paged workload
@@ -735,6 +742,83 @@ def gram_bench(args, spec, case):
         "measured_peaks": peaks,
         "kernels": {"gram": {"us": round(us, 2)}},
         "kernel_timing": "HIP events around the timed region / steps (one kernel per launch)",
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def kara_bench(args, spec, case, window_len=128, keep=32, anchors=4, radius=2):
+    """rkv_kara_step on the workload's caches: every sequence's last window_len
+    tokens are its uncompressed tail, scored by bidirectional attention of
+    their own queries and cut to `keep`.  Compaction is in place, so each step
+    gets a pristine cache copy prepared before the timed region; one event
+    pair around the back-to-back launches.  Algorithmic bytes per unit: the
+    window tokens' queries (G W d 2) and keys (W d 2) read once, scores
+    (W 4) and keep list (keep 4) written, moved K and V rows read and written."""
+    import numpy as np
+    import torch
+
+    import rkv_synth as syn
+    from gpu_harness import config_of, to_dev
+    from kv_cache_compression_decode_amd import binding as B
+
+    if spec.dtype != "bf16" or spec.layout != "contiguous":
+        raise SystemExit(f"{spec.name}: --kara times bf16 contiguous workloads")
+    steps = 50 if args.steps is None else args.steps
+    nsteps = args.warmup + steps
+    cfg = config_of(spec)
+    kc = B.rkv_kara_config(window_len, keep, anchors, radius)
+    lens0 = case.lens0.astype(np.int32)
+    tails0 = lens0 - window_len
+    q = to_dev(syn.build_queries(spec.with_(window=window_len)))
+    units = spec.num_seqs * spec.num_layers * spec.num_kv_heads
+    scores = torch.empty(units * window_len, dtype=torch.float32, device="cuda")
+    keep_t = torch.empty(units * keep, dtype=torch.int32, device="cuda")
+    copies = [(case.k.clone(), case.v.clone()) for _ in range(nsteps)]
+    caches = [B.make_cache(kk, vv, capacity=case.cap) for kk, vv in copies]
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        B.rkv_kara_step(cfg, kc, caches[i], q, spec.num_seqs, lens0.copy(), tails0.copy(), scores,
+                        keep_t, None, 0, None, None, 0, stream)
+
+    for i in range(args.warmup):
+        run(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.warmup, nsteps):
+        run(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    kept = keep_t.view(units, keep).cpu().numpy()
+    first = (lens0 - window_len)[0]
+    moved = int((kept != first + np.arange(keep)[None, :]).sum())
+    row = spec.head_dim * 2
+    nbytes = (units * (spec.group * window_len * row + window_len * row + window_len * 4 + keep * 4)
+              + moved * row * 2 * 2)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out = {
+        "metric": "KARA-style window steps/sec (score, Token2Chunk-select and compact every unit's window)",
+        "value": round(1e6 / us, 2), "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round((t1 - t0) * 1e3 / steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "num_seqs": spec.num_seqs, "num_layers": spec.num_layers,
+                   "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_dim": spec.head_dim, "seq_lens": sorted(set(int(x) for x in lens0)),
+                   "window_len": window_len, "keep": keep, "anchors": anchors, "radius": radius,
+                   "units": units},
+        "entry": "rkv_kara_step",
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("kara", spec.name),
+                     "kernel": "kara", "bytes_per_launch": nbytes},
+        "kernels": {"kara": {"us": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1)}},
+        "moved_rows": moved,
+        "kernel_timing": "HIP events around the timed region / steps (one kernel per step)",
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

@@ -337,6 +337,56 @@ rkv_status rkv_step_device(const rkv_config *cfg, const rkv_cache *cache, const 
                            int32_t *free_blocks, int32_t free_capacity, int32_t *d_free_counts,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* The KARA-style sliding-window variant (the KARA entry on the fugumt.com
+ * paper page, "KARA: Efficient Reasoning LLM Serving via Sliding-Window KV
+ * Cache Compression", Abstract: decode-time compression of only the recently
+ * generated context, bidirectional attention to score the window's KV pairs,
+ * Token2Chunk widening some of the selected pairs into chunks).  The
+ * abstract gives no formulas; this library reads it as follows. */
+typedef struct rkv_kara_config {
+  int32_t window_len;  /* W: the tail compressed at once (32, 64 or 128 tokens)   */
+  int32_t keep;        /* K in [1, W]: window tokens kept                         */
+  int32_t anchors;     /* m >= 0: the best tokens widened into chunks             */
+  int32_t radius;      /* r >= 0: a chunk is the positions within r of an anchor;
+                          m * (2 r + 1) <= K                                      */
+} rkv_kara_config;
+
+/* One KARA-style step.  A sequence triggers once its uncompressed tail
+ * (tokens from h_tail_start[s] on) holds W tokens; its window is then the
+ * last W tokens, t0 = len - W .. len - 1.  Per (sequence, layer, kv head):
+ *   score_j = mean over the G*W query rows (the window tokens' queries of the
+ *             G query heads that share the kv head) of softmax_j(q . k_j /
+ *             sqrt(d)) over the W window keys -- bidirectional: no causal mask;
+ *   keep    = the chunks [a - r, a + r] (clipped to the window) of the m best
+ *             tokens a, then the best tokens outside those chunks until K
+ *             places are filled (equal scores: lower position first);
+ *   slots t0 .. t0 + K - 1 of K and V receive the kept tokens' rows in
+ *   position order; the prefix [0, t0) is not touched.
+ * Then h_seq_lens[s] = h_tail_start[s] = t0 + K.  Every kv head keeps its own
+ * set.  cfg gives the model and cache shape (bf16 caches; budget, buffer,
+ * window, mix_lambda and shared_selection are not used).
+ *   q_tail        device bf16 [num_layers][num_seqs][num_q_heads][W][head_dim]:
+ *                 the queries of the window tokens, any order within a head
+ *                 (rkv_window_store with window = W keeps them)
+ *   h_seq_lens, h_tail_start  host int32 [num_seqs], in/out
+ *   scores        device float32 [num_layers][num_seqs][num_kv_heads][W]
+ *   keep          device int32 [num_layers][num_seqs][num_kv_heads][K]: the
+ *                 kept tokens' positions (t0 + window index), ascending
+ *   free_blocks   paged: ids of logical blocks ceil((t0+K)/bs) ..
+ *                 ceil(len/bs) - 1, sequences in order; h_free_counts as for
+ *                 rkv_compact
+ *   workspace     NULL, or >= 256 bytes (256-byte aligned) whose status word
+ *                 records a failed block-id check; required with
+ *                 cfg->check_block_table = 1
+ * Rows, scores and keep entries of sequences that do not trigger are not
+ * written.  Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED (float32, W,
+ * head_dim, length above RKV_MAX_LEN), RKV_ERR_WORKSPACE, RKV_ERR_HIP. */
+rkv_status rkv_kara_step(const rkv_config *cfg, const rkv_kara_config *kc, const rkv_cache *cache,
+                         const void *q_tail, int32_t num_seqs, int32_t *h_seq_lens,
+                         int32_t *h_tail_start, float *scores, int32_t *keep,
+                         int32_t *free_blocks, int32_t free_capacity, int32_t *h_free_counts,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 /* rkv_step without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments as rkv_step minus the workspace, same

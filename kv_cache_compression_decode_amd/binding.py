@@ -39,7 +39,7 @@ EXPORTS = ("rkv_status_string", "rkv_last_error", "rkv_is_triggered", "rkv_works
            "rkv_redundancy_gram", "rkv_window_store",
            "rkv_score", "rkv_select", "rkv_compact", "rkv_step",
            "rkv_step_device_workspace_size", "rkv_step_device", "rkv_device_status",
-           "rkv_set_span_wait_us", "rkv_step_noalloc")
+           "rkv_set_span_wait_us", "rkv_step_noalloc", "rkv_kara_step")
 
 
 class rkv_config(ctypes.Structure):
@@ -55,6 +55,11 @@ class rkv_cache(ctypes.Structure):
                 ("capacity", c_int32),
                 ("num_blocks", c_int32), ("block_table", c_void_p),
                 ("max_blocks_per_seq", c_int32)]
+
+
+class rkv_kara_config(ctypes.Structure):
+    _fields_ = [("window_len", c_int32), ("keep", c_int32), ("anchors", c_int32),
+                ("radius", c_int32)]
 
 
 class RkvError(RuntimeError):
@@ -114,6 +119,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_int32, c_void_p, c_void_p, c_int32, P(c_int32),
                                      c_void_p]
     lib.rkv_step_noalloc.restype = c_int32
+    lib.rkv_kara_step.argtypes = [P(rkv_config), P(rkv_kara_config), P(rkv_cache), c_void_p, c_int32,
+                                  P(c_int32), P(c_int32), c_void_p, c_void_p, c_void_p, c_int32,
+                                  P(c_int32), c_void_p, c_size_t, c_void_p]
+    lib.rkv_kara_step.restype = c_int32
     lib.rkv_device_status.argtypes = [c_void_p, c_void_p, P(ctypes.c_uint32)]
     lib.rkv_device_status.restype = c_int32
     lib.rkv_set_span_wait_us.argtypes = [ctypes.c_int64]
@@ -276,6 +285,24 @@ def rkv_step_noalloc(cfg, cache, q_window, num_seqs, seq_lens: np.ndarray, score
                                    num_seqs, _i32p(seq_lens), _ptr(scores), score_stride,
                                    _ptr(keep), _ptr(free_blocks), free_capacity,
                                    _i32p(free_counts), _stream(stream)))
+
+
+def rkv_kara_step(cfg, kc, cache, q_tail, num_seqs, seq_lens: np.ndarray, tail_start: np.ndarray,
+                  scores, keep, free_blocks=None, free_capacity=0,
+                  free_counts: Optional[np.ndarray] = None, workspace=None, workspace_bytes=0,
+                  stream=None) -> None:
+    """seq_lens and tail_start (C-contiguous int32 numpy) are updated in place."""
+    for name, arr in (("seq_lens", seq_lens), ("tail_start", tail_start)):
+        if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
+            raise TypeError(f"{name} must be a C-contiguous int32 numpy array (updated in place)")
+    if free_counts is not None and not (free_counts.dtype == np.int32
+                                        and free_counts.flags.c_contiguous):
+        raise TypeError("free_counts must be a C-contiguous int32 numpy array")
+    _check(load().rkv_kara_step(ctypes.byref(cfg), ctypes.byref(kc), ctypes.byref(cache),
+                                _ptr(q_tail), num_seqs, _i32p(seq_lens), _i32p(tail_start),
+                                _ptr(scores), _ptr(keep), _ptr(free_blocks), free_capacity,
+                                _i32p(free_counts), _ptr(workspace), workspace_bytes,
+                                _stream(stream)))
 
 
 def rkv_device_status(workspace, stream=None) -> int:

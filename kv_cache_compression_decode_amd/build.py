@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["rkv_api.hip", "rkv_score.hip", "rkv_select.hip", "rkv_compact.hip", "rkv_table.hip",
-           "rkv_gram.hip", "rkv_window.hip"] + [
+           "rkv_gram.hip", "rkv_window.hip", "rkv_kara.hip"] + [
     f"rkv_score_{dt}_d{d}_{lay}.hip" for dt in ("bf16", "f32") for d in (64, 128)
     for lay in ("contig", "paged")]
 

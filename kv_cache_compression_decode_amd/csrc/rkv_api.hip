@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "rkv.h"
+#include "rkv_kara.h"
 #include "rkv_launch.h"
 
 namespace {
@@ -50,19 +51,14 @@ int ilog2_exact(int v) {
   return s;
 }
 
-rkv_status check_config(const rkv_config* c) {
+// The model and cache shape of a config (every entry point).
+rkv_status check_shape(const rkv_config* c) {
   if (c == nullptr) return fail(RKV_ERR_INVALID_ARG, "cfg is NULL");
   if (c->num_layers < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1)
     return fail(RKV_ERR_INVALID_ARG, "num_layers, num_q_heads and num_kv_heads must be >= 1");
   if (c->num_q_heads % c->num_kv_heads != 0)
     return fail(RKV_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                 c->num_q_heads, c->num_kv_heads);
-  if (c->window < 1) return fail(RKV_ERR_INVALID_ARG, "window must be >= 1");
-  if (c->budget <= c->window)
-    return fail(RKV_ERR_INVALID_ARG, "budget (%d) must exceed window (%d)", c->budget, c->window);
-  if (c->buffer < 1) return fail(RKV_ERR_INVALID_ARG, "buffer must be >= 1");
-  if (!(c->mix_lambda >= 0.f && c->mix_lambda <= 1.f))
-    return fail(RKV_ERR_INVALID_ARG, "mix_lambda must lie in [0, 1]");
   if (c->dtype != RKV_DTYPE_F32 && c->dtype != RKV_DTYPE_BF16)
     return fail(RKV_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
   if (c->layout != RKV_LAYOUT_CONTIGUOUS && c->layout != RKV_LAYOUT_PAGED)
@@ -75,6 +71,20 @@ rkv_status check_config(const rkv_config* c) {
       return fail(RKV_ERR_UNSUPPORTED, "block_size %d (supported: powers of two up to 1024)",
                   c->block_size);
   }
+  if (c->check_block_table != 0 && c->check_block_table != 1)
+    return fail(RKV_ERR_INVALID_ARG, "check_block_table must be 0 or 1");
+  return RKV_OK;
+}
+
+rkv_status check_config(const rkv_config* c) {
+  rkv_status st = check_shape(c);
+  if (st != RKV_OK) return st;
+  if (c->window < 1) return fail(RKV_ERR_INVALID_ARG, "window must be >= 1");
+  if (c->budget <= c->window)
+    return fail(RKV_ERR_INVALID_ARG, "budget (%d) must exceed window (%d)", c->budget, c->window);
+  if (c->buffer < 1) return fail(RKV_ERR_INVALID_ARG, "buffer must be >= 1");
+  if (!(c->mix_lambda >= 0.f && c->mix_lambda <= 1.f))
+    return fail(RKV_ERR_INVALID_ARG, "mix_lambda must lie in [0, 1]");
   const long gw = (long)(c->num_q_heads / c->num_kv_heads) * c->window;
   if (gw > RKV_MAX_WINDOW_ROWS)
     return fail(RKV_ERR_UNSUPPORTED, "group * window = %ld exceeds %d", gw, RKV_MAX_WINDOW_ROWS);
@@ -82,8 +92,6 @@ rkv_status check_config(const rkv_config* c) {
     return fail(RKV_ERR_UNSUPPORTED, "budget %d exceeds %d", c->budget, RKV_MAX_LEN);
   if (c->shared_selection != 0 && c->shared_selection != 1)
     return fail(RKV_ERR_INVALID_ARG, "shared_selection must be 0 or 1");
-  if (c->check_block_table != 0 && c->check_block_table != 1)
-    return fail(RKV_ERR_INVALID_ARG, "check_block_table must be 0 or 1");
   return RKV_OK;
 }
 
@@ -836,6 +844,101 @@ rkv_status rkv_step_noalloc(const rkv_config* cfg, const rkv_cache* cache, const
     return fail(RKV_ERR_WORKSPACE, "the step needs more scratch than the %zu bytes rkv_step_noalloc holds (%s)",
                 kScratchBytes, g_err.c_str());
   return st;
+}
+
+rkv_status rkv_kara_step(const rkv_config* cfg, const rkv_kara_config* kc, const rkv_cache* cache,
+                         const void* q_tail, int32_t num_seqs, int32_t* h_seq_lens,
+                         int32_t* h_tail_start, float* scores, int32_t* keep, int32_t* free_blocks,
+                         int32_t free_capacity, int32_t* h_free_counts, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  rkv_status st = check_shape(cfg);
+  if (st != RKV_OK) return st;
+  if (cfg->dtype != RKV_DTYPE_BF16) return fail(RKV_ERR_UNSUPPORTED, "rkv_kara_step takes bf16 caches");
+  if (kc == nullptr) return fail(RKV_ERR_INVALID_ARG, "kara config is NULL");
+  const int W = kc->window_len, K = kc->keep;
+  if (W != 32 && W != 64 && W != 128)
+    return fail(RKV_ERR_UNSUPPORTED, "window_len %d (supported: 32, 64, 128)", W);
+  if (K < 1 || K > W) return fail(RKV_ERR_INVALID_ARG, "keep %d outside [1, window_len %d]", K, W);
+  if (kc->anchors < 0 || kc->radius < 0)
+    return fail(RKV_ERR_INVALID_ARG, "anchors and radius must be >= 0");
+  if ((long)kc->anchors * (2L * kc->radius + 1) > K)
+    return fail(RKV_ERR_INVALID_ARG, "anchors * (2 radius + 1) = %ld exceeds keep %d",
+                (long)kc->anchors * (2L * kc->radius + 1), K);
+  if ((st = check_cache(cfg, cache, true, num_seqs)) != RKV_OK) return st;
+  if (num_seqs < 0) return fail(RKV_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs > 0 && (h_seq_lens == nullptr || h_tail_start == nullptr))
+    return fail(RKV_ERR_INVALID_ARG, "h_seq_lens and h_tail_start must not be NULL");
+  const bool paged = cfg->layout == RKV_LAYOUT_PAGED;
+  const bool check = checks_blocks(cfg);
+  std::vector<Trig> trig;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t n = h_seq_lens[s], tail = h_tail_start[s];
+    if (n < 0 || tail < 0 || tail > n)
+      return fail(RKV_ERR_INVALID_ARG, "sequence %d: length %d, tail start %d", s, n, tail);
+    if ((long)n - tail < W) continue;
+    if (n > RKV_MAX_LEN) return fail(RKV_ERR_UNSUPPORTED, "h_seq_lens[%d] = %d exceeds %d", s, n, RKV_MAX_LEN);
+    if (!paged && n > cache->capacity)
+      return fail(RKV_ERR_INVALID_ARG, "h_seq_lens[%d] = %d exceeds capacity %d", s, n, cache->capacity);
+    if (paged && (long)n > (long)cache->max_blocks_per_seq * cfg->block_size)
+      return fail(RKV_ERR_INVALID_ARG, "h_seq_lens[%d] = %d exceeds the block table (%d blocks)", s, n,
+                  cache->max_blocks_per_seq);
+    trig.push_back({s, n});
+  }
+  std::vector<int32_t> counts(num_seqs > 0 ? num_seqs : 0, 0), offs(trig.size(), 0);
+  long total = 0;
+  if (paged) {
+    const long bs = cfg->block_size;
+    for (size_t i = 0; i < trig.size(); ++i) {
+      const long n = trig[i].len, n_new = n - W + K;
+      counts[trig[i].seq] = (int32_t)((n + bs - 1) / bs - (n_new + bs - 1) / bs);
+      offs[i] = (int32_t)total;
+      total += counts[trig[i].seq];
+    }
+    if (total > 0 && free_blocks == nullptr) return fail(RKV_ERR_INVALID_ARG, "free_blocks is NULL");
+    if (total > free_capacity)
+      return fail(RKV_ERR_INVALID_ARG, "free_capacity %d below the %ld freed blocks", free_capacity, total);
+  }
+  if (!trig.empty()) {
+    if (q_tail == nullptr) return fail(RKV_ERR_INVALID_ARG, "q_tail is NULL");
+    if (!aligned16(q_tail)) return fail(RKV_ERR_INVALID_ARG, "q_tail must be 16-byte aligned");
+    if (scores == nullptr || keep == nullptr) return fail(RKV_ERR_INVALID_ARG, "scores and keep must not be NULL");
+    if (check && workspace == nullptr) return fail(RKV_ERR_WORKSPACE, "check_block_table needs a workspace");
+    if (workspace != nullptr && (st = check_ws(workspace, workspace_bytes, kStatusBytes)) != RKV_OK)
+      return st;
+    rkv::KaraArgs a{};
+    a.g = make_geom(cfg, cache, num_seqs);
+    a.q = q_tail;
+    a.k = cache->k;
+    a.v = cache->v;
+    a.bt = cache->block_table;
+    a.scores = scores;
+    a.keep_out = keep;
+    a.free_blocks = paged ? free_blocks : nullptr;
+    a.status = check ? status_of(workspace) : nullptr;
+    a.window_len = W;
+    a.keep = K;
+    a.anchors = kc->anchors;
+    a.radius = kc->radius;
+    a.c = (float)(1.4426950408889634 / sqrt((double)cfg->head_dim));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (size_t first = 0; first < trig.size(); first += rkv::kMaxTrig) {
+      const int cnt = (int)std::min<size_t>(rkv::kMaxTrig, trig.size() - first);
+      fill_table(a.tt, trig, first, cnt, offs.data());
+      a.g.num_trig = cnt;
+      hipError_t e;
+      if (check && (e = prologue(a.g, a.tt, workspace, cache, first == 0, true, hs)) != hipSuccess)
+        return hip_fail(e, "prologue launch");
+      if ((e = rkv::launch_kara(a, hs)) != hipSuccess) return hip_fail(e, "kara launch");
+    }
+  }
+  for (const Trig& t : trig) {
+    h_seq_lens[t.seq] = t.len - W + K;
+    h_tail_start[t.seq] = t.len - W + K;
+  }
+  if (h_free_counts != nullptr)
+    for (int32_t s = 0; s < num_seqs; ++s) h_free_counts[s] = counts[s];
+  return RKV_OK;
 }
 
 rkv_status rkv_device_status(const void* workspace, void* stream, uint32_t* flags) {

@@ -50,7 +50,8 @@ def test_struct_layouts(tmp_path):
     gives the header's structures (gcc, host only)."""
     import subprocess
     fields = {"rkv_config": [f[0] for f in B.rkv_config._fields_],
-              "rkv_cache": [f[0] for f in B.rkv_cache._fields_]}
+              "rkv_cache": [f[0] for f in B.rkv_cache._fields_],
+              "rkv_kara_config": [f[0] for f in B.rkv_kara_config._fields_]}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rkv.h"', 'int main(void) {']
     for st, names in fields.items():
         lines.append(f'  printf("{st} size %zu\\n", sizeof({st}));')
@@ -64,7 +65,8 @@ def test_struct_layouts(tmp_path):
                    check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
     got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
-    for st, cls in (("rkv_config", B.rkv_config), ("rkv_cache", B.rkv_cache)):
+    for st, cls in (("rkv_config", B.rkv_config), ("rkv_cache", B.rkv_cache),
+                    ("rkv_kara_config", B.rkv_kara_config)):
         assert got[(st, "size")] == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert got[(st, f)] == getattr(cls, f).offset, (st, f)
@@ -362,3 +364,36 @@ def test_membench_library_exports_its_header():
     assert lib.rkv_membench_read(FAKE, 17, FAKE, 0, None) == -1
     assert lib.rkv_membench_copy(FAKE, FAKE, 8, 0, None) == -1
     assert lib.rkv_membench_copy(FAKE, FAKE, 0, 0, None) == 0       # nothing to do
+
+
+def kara(c, kc, ca=None, lens=(1152,), tails=(1024,), q=FAKE, scores=FAKE, keep=FAKE, fb=None, cap=0,
+         ws=None, wsb=0):
+    B.rkv_kara_step(c, kc, cache() if ca is None else ca, q, len(lens), np.array(lens, np.int32),
+                    np.array(tails, np.int32), scores, keep, fb, cap, None, ws, wsb, None)
+
+
+def test_kara_argument_errors():
+    """rkv_kara_step checks everything before it enqueues anything."""
+    c = cfg()
+    good = B.rkv_kara_config(128, 32, 4, 2)
+    expect(B.RKV_ERR_UNSUPPORTED, kara, cfg(dtype="f32"), good)
+    expect(B.RKV_ERR_UNSUPPORTED, kara, c, B.rkv_kara_config(96, 32, 4, 2))
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, B.rkv_kara_config(128, 0, 0, 0))
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, B.rkv_kara_config(128, 129, 0, 0))
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, B.rkv_kara_config(128, 32, 4, 4))   # 4 * 9 > 32
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, B.rkv_kara_config(128, 32, -1, 0))
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, good, tails=(1200,))               # tail past the end
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, good, q=None)
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, good, keep=None)
+    expect(B.RKV_ERR_INVALID_ARG, kara, c, good, ca=cache(capacity=1000))
+    pc = cfg(layout="paged")
+    pca = cache(num_blocks=100, block_table=FAKE, max_blocks=72)
+    # 1152 -> 1056 tokens at bs 16: 72 -> 66 blocks, 6 freed
+    expect(B.RKV_ERR_INVALID_ARG, kara, pc, good, ca=pca, fb=FAKE, cap=5)
+    pc.check_block_table = 1
+    expect(B.RKV_ERR_WORKSPACE, kara, pc, good, ca=pca, fb=FAKE, cap=6)
+    # below the trigger nothing is enqueued and nothing changes
+    lens = np.array([1151, 100], np.int32)
+    tails = np.array([1024, 0], np.int32)
+    B.rkv_kara_step(c, good, cache(), None, 2, lens, tails, None, None, None, 0, None, None, 0, None)
+    assert list(lens) == [1151, 100] and list(tails) == [1024, 0]
