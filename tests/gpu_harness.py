@@ -215,6 +215,61 @@ def check_unit(case, step, s, l, h, tag=""):
     return len(diff)
 
 
+def unit_job_inputs(case, step, s, l, h):
+    """Everything check_unit compares, as plain numpy arrays (for a worker)."""
+    spec = case.spec
+    n = int(case.lens0[s])
+    krows, vrows = case.unit_rows(s, l, h)
+    g = unit_outputs(step, spec, s, l, h, n)
+    gk, gv = case.gpu_rows(s, l, h, spec.budget)
+    return dict(where=f"unit (s={s}, l={l}, h={h}) N={n}", dtype=spec.dtype,
+                hq=spec.num_q_heads, hkv=spec.num_kv_heads, budget=spec.budget,
+                window=spec.window, lam=spec.mix_lambda, h=h, q=case.q_host[l, s],
+                krows=np.ascontiguousarray(krows), vrows=np.ascontiguousarray(vrows),
+                score=g["score"], keep=g["keep"], imp=g.get("imp"), red=g.get("red"), gk=gk, gv=gv)
+
+
+def check_units_parallel(case, step, units, tag, workers=12):
+    """check_unit for many units, the oracle in worker processes that import
+    numpy and the oracle only (oracle_jobs.run_jobs); inputs gathered here."""
+    import oracle_jobs
+    jobs = (unit_job_inputs(case, step, s, l, h) for (s, l, h) in units)
+    near, errors = oracle_jobs.run_jobs(jobs, workers)
+    assert not errors, f"{tag}: {len(errors)} units differ, first: {errors[0]}"
+    log(f"{tag}: {len(units)} units match the oracle ({near} keep differences inside the band)")
+    return near
+
+
+def one_unit_per_layer(spec, seed=0, triggered=None):
+    """One (sequence, layer) pair's unit for every triggered sequence and
+    layer, the kv head drawn at random."""
+    lens = syn.seq_lens(spec)
+    rng = np.random.default_rng([992, seed])
+    return [(s, l, int(rng.integers(spec.num_kv_heads)))
+            for s in range(spec.num_seqs) if lens[s] >= spec.budget + spec.buffer
+            and (triggered is None or s in triggered) for l in range(spec.num_layers)]
+
+
+def keep_invariants_on_device(step, spec, lens):
+    """Every triggered unit's keep row: budget entries, strictly ascending,
+    inside [0, N), the window last (checked on the GPU for all units)."""
+    B_, w = spec.budget, spec.window
+    keep = step.keep.view(spec.num_layers, spec.num_seqs, spec.num_kv_heads, B_).long()
+    count = 0
+    for s in range(spec.num_seqs):
+        n = int(lens[s])
+        if n < spec.budget + spec.buffer:
+            continue
+        ks = keep[:, s]
+        assert bool((ks[..., 1:] > ks[..., :-1]).all()), f"seq {s}: a keep row is not ascending"
+        assert bool((ks[..., 0] >= 0).all()) and bool((ks[..., -1] == n - 1).all())
+        win = torch.arange(n - w, n, device=ks.device)
+        assert bool((ks[..., B_ - w:] == win).all()), f"seq {s}: the window is not kept last"
+        assert bool((ks[..., B_ - w - 1] < n - w).all())
+        count += spec.num_layers * spec.num_kv_heads
+    return count
+
+
 def check_layer_shared(case, step, s, l, tag=""):
     """Head-shared selection for one (sequence, layer): every head's scores
     within tolerance of the oracle; one keep row shared by all heads, equal to

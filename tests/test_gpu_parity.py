@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import rkv_synth as syn
-from gpu_harness import (ContigCase, PagedCase, check_unit, config_of, log, make_case, run_step,
+from gpu_harness import (ContigCase, PagedCase, check_unit, check_units_parallel, config_of,
+                         keep_invariants_on_device, log, make_case, one_unit_per_layer, run_step,
                          sample_units, to_host)
 from kv_cache_compression_decode_amd import binding as B
 
@@ -180,7 +181,8 @@ def test_config2_ragged_literal():
     trig = [s for s in range(spec.num_seqs) if case.lens0[s] >= spec.budget + spec.buffer]
     log(f"config 2 at seed {spec.seed}: lengths {case.lens0.tolist()}, triggered {trig}")
     check_untriggered(case, step, lens)
-    check_all(case, step, sample_units(spec, 24), "qwen7b-ragged16")
+    # every unit of the triggered sequence (28 layers x 4 kv heads)
+    check_units_parallel(case, step, sample_units(spec, 10**9), "qwen7b-ragged16")
 
 
 @pytest.mark.timeout(600)
@@ -191,7 +193,9 @@ def test_config2_all_triggered_diagnostic():
     case = ContigCase(spec)
     step, lens = run_step(case)
     assert (lens == spec.budget).all()
-    check_all(case, step, sample_units(spec, 40, seed=2), "ragged-all-trigger")
+    # one unit per (sequence, layer): 448 units
+    check_units_parallel(case, step, one_unit_per_layer(spec, seed=2), "ragged-all-trigger")
+    assert keep_invariants_on_device(step, spec, case.lens0) == 16 * 28 * 4
     check_tail_untouched(case)
 
 
@@ -200,11 +204,33 @@ def test_config3_paged_full():
     spec = syn.config(3)
     log("config 3: building 128 GiB of pools")
     case = PagedCase(spec)
+    ref_blocks = torch.from_numpy(np.unique(case.bt).astype(np.int64)).to(case.k.device)
+    pristine_k = case.k.index_select(1, ref_blocks)
+    pristine_v = case.v.index_select(1, ref_blocks)
     log("config 3: running the step")
     step, lens = run_step(case)
     check_free_blocks(case, step)
     assert len(step.free_counts) == 8 and all(c == 16 for c in step.free_counts)
-    check_all(case, step, sample_units(spec, 12, seed=3), "llama8b-paged8")
+    assert keep_invariants_on_device(step, spec, case.lens0) == 2048
+    # one unit per (sequence, layer) against the oracle: 256 units
+    check_units_parallel(case, step, one_unit_per_layer(spec, seed=3), "llama8b-paged8")
+    # every unit's compacted rows against a gather of the pristine blocks
+    pos = {int(b): i for i, b in enumerate(ref_blocks.tolist())}
+    keep = step.keep.view(spec.num_layers, spec.num_seqs, spec.num_kv_heads, spec.budget).long()
+    bs, nkeep = spec.block_size, spec.budget // spec.block_size
+    for s in range(spec.num_seqs):
+        nb = -(-int(case.lens0[s]) // bs)
+        src = torch.tensor([pos[int(b)] for b in case.bt[s, :nb]], device=case.k.device)
+        dst = torch.from_numpy(case.bt[s, :nkeep].astype(np.int64)).to(case.k.device)
+        for pool, pristine in ((case.k, pristine_k), (case.v, pristine_v)):
+            for l in range(spec.num_layers):
+                # logical rows of every kv head: (H, nb * bs, d)
+                old = pristine[l].index_select(0, src).permute(1, 0, 2, 3).reshape(spec.num_kv_heads, nb * bs, -1)
+                want = torch.gather(old, 1, keep[l, s].unsqueeze(-1).expand(-1, -1, old.shape[-1]))
+                got = pool[l].index_select(0, dst).permute(1, 0, 2, 3).reshape(spec.num_kv_heads, nkeep * bs, -1)
+                assert torch.equal(got, want), (s, l)
+    log("config 3: all 2048 units compacted as their keep lists say")
+    del pristine_k, pristine_v
     # blocks nobody references still hold the canary
     ref = np.zeros(spec.num_blocks, dtype=bool)
     ref[case.bt.ravel()] = True
@@ -225,7 +251,9 @@ def test_config4_70b_full():
     v0 = case.v.clone()
     log("config 4: running the step")
     step, lens = run_step(case, keep_parts=False)
-    check_all(case, step, sample_units(spec, 16, seed=4), "70b-batch32")
+    assert keep_invariants_on_device(step, spec, case.lens0) == 20480
+    # one unit per (sequence, layer) against the oracle: 2560 units
+    check_units_parallel(case, step, one_unit_per_layer(spec, seed=4), "70b-batch32")
     # property at full size: every compacted row is the original row keep[i]
     keep = step.keep.view(spec.num_layers, spec.num_seqs, spec.num_kv_heads, spec.budget).long()
     for l in range(spec.num_layers):
