@@ -793,6 +793,11 @@ def kara_bench(args, spec, case, window_len=128, keep=32, anchors=4, radius=2):
     ev[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
     kept = keep_t.view(units, keep).cpu().numpy()
     first = (lens0 - window_len)[0]

@@ -66,9 +66,9 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   static_assert((W * PPR + kWave) * 16 <= (kThreads / kWave) * kRing * TILE_BYTES, "compaction buffer");
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][kRing][TILE_BYTES];
   __shared__ float part[WAVES][W];
-  __shared__ uint32_t okey[W];
+  __shared__ __attribute__((aligned(16))) uint32_t okey[W];
+  __shared__ __attribute__((aligned(16))) uint32_t okey2[W];   // 0 for tokens inside a chunk
   __shared__ int rank1[W];
-  __shared__ uint8_t in_chunk[W];
   __shared__ int keep_s[W];
   __shared__ int tot[WAVES];
 
@@ -182,34 +182,32 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   __syncthreads();
 
   // Token2Chunk: rank by (score desc, position asc); the `anchors` best are
-  // widened to +-radius; the other places go to the best outside the chunks
+  // widened to +-radius; the other places go to the best outside the chunks.
+  // Ranks by counting, every thread reading all W keys (broadcast reads, four
+  // at a time).  Scores are softmax means, so every order key is at least
+  // 0x80000000 and a chunk token's key in okey2, 0, beats no other token.
   const int K = a.keep;
-  uint32_t kt = 0;
-  if (t < W) {
-    kt = okey[t];
-    int r1 = 0;
-    for (int i = 0; i < W; ++i) {
-      const uint32_t ki = okey[i];
-      r1 += ki > kt || (ki == kt && i < t);
+  auto count_beating = [&](const uint32_t* keys, uint32_t kt) {
+    int r = 0;
+#pragma unroll 8
+    for (int i = 0; i < W; i += 4) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
+      r += (k4.x > kt || (k4.x == kt && i < t)) + (k4.y > kt || (k4.y == kt && i + 1 < t)) +
+           (k4.z > kt || (k4.z == kt && i + 2 < t)) + (k4.w > kt || (k4.w == kt && i + 3 < t));
     }
-    rank1[t] = r1;
-  }
+    return r;
+  };
+  const uint32_t kt = t < W ? okey[t] : 0u;
+  if (t < W) rank1[t] = count_beating(okey, kt);
   __syncthreads();
   bool chunk = false;
   if (t < W) {
     for (int i = max(0, t - a.radius); i <= min(W - 1, t + a.radius); ++i) chunk |= rank1[i] < a.anchors;
-    in_chunk[t] = chunk ? 1 : 0;
+    okey2[t] = chunk ? 0u : kt;
   }
   const int nchunk = __syncthreads_count(t < W && chunk);
   bool kept = chunk;
-  if (t < W && !chunk) {
-    int r2 = 0;
-    for (int i = 0; i < W; ++i) {
-      const uint32_t ki = okey[i];
-      r2 += !in_chunk[i] && (ki > kt || (ki == kt && i < t));
-    }
-    kept = r2 < K - nchunk;
-  }
+  if (t < W && !chunk) kept = count_beating(okey2, kt) < K - nchunk;
   // slot of each kept position: a workgroup scan of the flags
   const int slot = block_excl_scan<kThreads>(t < W && kept ? 1 : 0, tot);
   int32_t* krow = a.keep_out + orow * K;
