@@ -583,6 +583,8 @@ def three_call_record(spec, case, step, copies, caches, stream, reps=10):
     for name in ("score", "select"):   # warm-up: the first launch of a kernel loads it
         calls[name](0)
     step.compact(caches[0], lens0.copy(), stream)   # copy 0 is the compaction's warm-up
+    copies[0][0].copy_(case.k)                      # and is the scoring's input again
+    copies[0][1].copy_(case.v)
     torch.cuda.synchronize()
     for j, name in enumerate(("score", "select", "compact")):
         ev[2 * j].record(stream)
@@ -754,7 +756,8 @@ def kara_bench(args, spec, case, window_len=128, keep=32, anchors=4, radius=2):
     gets a pristine cache copy prepared before the timed region; one event
     pair around the back-to-back launches.  Algorithmic bytes per unit: the
     window tokens' queries (G W d 2) and keys (W d 2) read once, scores
-    (W 4) and keep list (keep 4) written, moved K and V rows read and written."""
+    (W 4) and keep list (keep 4) written; per moved row, its K row written
+    (the keys were read for the scores) and its V row read and written."""
     import numpy as np
     import torch
 
@@ -803,8 +806,10 @@ def kara_bench(args, spec, case, window_len=128, keep=32, anchors=4, radius=2):
     first = (lens0 - window_len)[0]
     moved = int((kept != first + np.arange(keep)[None, :]).sum())
     row = spec.head_dim * 2
+    # the window keys are read once (for the scores); a moved row's K is
+    # written, its V read and written
     nbytes = (units * (spec.group * window_len * row + window_len * row + window_len * 4 + keep * 4)
-              + moved * row * 2 * 2)
+              + moved * row * 3)
     gbs = nbytes / (us * 1e-6) / 1e9
     out = {
         "metric": "KARA-style window steps/sec (score, Token2Chunk-select and compact every unit's window)",

@@ -24,9 +24,12 @@
 // an LDS pass over the four waves give the scores.  Query tiles reach the
 // MFMA operands through a ring in LDS filled by global_load_lds, so loads of
 // the next tiles are in flight without holding registers.  Selection ranks the W
-// tokens by counting (W <= 128: one thread per token).  Compaction stages
-// every kept row in LDS before any is written (keep[i] >= i).
-// Window lengths 32, 64 and 128 are compiled.
+// tokens by counting (W <= 128: one thread per token).  Compaction needs no
+// read after the selection: the window's V rows are copied into LDS by
+// global_load_lds at the start (the copies land during the scoring) and
+// its K rows are the MFMA operands already in registers, so every kept row
+// is written from on-chip copies (keep[i] >= i: nothing is overwritten
+// before it is read).  Window lengths 32, 64 and 128 are compiled.
 #include "rkv_kara.h"
 #include "rkv_score_impl.h"
 #include "rkv_select_impl.h"
@@ -61,16 +64,19 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   constexpr int TILE_BYTES = 16 * D * 2;              // 16 query rows
   constexpr int NI = TILE_BYTES / (kWave * 16);       // wave-wide 16-byte loads per tile
   constexpr int WAVES = kThreads / kWave;
+  constexpr int VI = W * PPR / kThreads;              // wave-wide 16-byte loads per wave for the V rows
   static_assert(W <= kKaraMaxW, "window");
-  // the compaction stages up to W rows (+ one wave's overhang) in the ring
-  static_assert((W * PPR + kWave) * 16 <= (kThreads / kWave) * kRing * TILE_BYTES, "compaction buffer");
+  static_assert(VI >= 1 && VI * kThreads == W * PPR, "V rows in whole wave-wide loads");
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][kRing][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vwin[W * PPR * 16];   // the window's V rows
   __shared__ float part[WAVES][W];
   __shared__ __attribute__((aligned(16))) uint32_t okey[W];
-  __shared__ __attribute__((aligned(16))) uint32_t okey2[W];   // 0 for tokens inside a chunk
+  __shared__ uint64_t xchg[W];   // bitonic exchange across the two waves
   __shared__ int rank1[W];
+  __shared__ int kflag[W];
   __shared__ int keep_s[W];
-  __shared__ int tot[WAVES];
+  __shared__ int slot_of[W];
+  __shared__ int tot[WAVES], tot2[WAVES];
 
   const Unit u = decode_unit(a.g, a.tt, blockIdx.x);
   if (u.n == 0) return;
@@ -81,6 +87,14 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
 
   KeyRows<PAGED> rows;
   rows.init(a.g, a.bt, u);
+  // the window's V rows into LDS (piece p of row r at r * PPR + p); these are
+  // the oldest loads of every wave, so each wait below also covers them
+  uint8_t* const vbase = reinterpret_cast<uint8_t*>(a.v);
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int s0 = (wave * VI + i) * kWave, sp = s0 + lane;
+    tile_piece_to_lds(vbase + rows.at(t0 + sp / PPR) * 2 + (sp % PPR) * 16, vwin + s0 * 16);
+  }
   // the W window keys: block j holds key j*16 + col, dims 32 ks + 8 g4 .. +7
   KeyFrag<true, D> kf[NB];
 #pragma unroll
@@ -183,64 +197,79 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
 
   // Token2Chunk: rank by (score desc, position asc); the `anchors` best are
   // widened to +-radius; the other places go to the best outside the chunks.
-  // Ranks by counting, every thread reading all W keys (broadcast reads, four
-  // at a time).  Scores are softmax means, so every order key is at least
-  // 0x80000000 and a chunk token's key in okey2, 0, beats no other token.
+  // A bitonic sort of the W composite keys (order key, then 255 - position:
+  // unique, larger is better), one per thread of the first W, exchanges
+  // through lane shuffles (partner distance < 64) or LDS (64).  Sorted index
+  // = rank.  The fill takes the first K - |chunks| non-chunk tokens in that
+  // order (a scan over the sorted positions).
   const int K = a.keep;
-  auto count_beating = [&](const uint32_t* keys, uint32_t kt) {
-    int r = 0;
-#pragma unroll 8
-    for (int i = 0; i < W; i += 4) {
-      const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
-      r += (k4.x > kt || (k4.x == kt && i < t)) + (k4.y > kt || (k4.y == kt && i + 1 < t)) +
-           (k4.z > kt || (k4.z == kt && i + 2 < t)) + (k4.w > kt || (k4.w == kt && i + 3 < t));
+  uint64_t ck = t < W ? ((uint64_t)okey[t] << 8) | (uint64_t)(255 - t) : 0ull;
+#pragma unroll
+  for (int kk = 2; kk <= W; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      uint64_t other;
+      if (j < kWave) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)ck, j);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(ck >> 32), j);
+        other = ((uint64_t)hi << 32) | lo;
+      } else {
+        __syncthreads();
+        if (t < W) xchg[t] = ck;
+        __syncthreads();
+        other = t < W ? xchg[t ^ j] : 0ull;
+      }
+      // descending within blocks of kk whose index bit kk is clear
+      const bool desc = (t & kk) == 0, lower = (t & j) == 0;
+      const uint64_t hi_v = ck > other ? ck : other, lo_v = ck > other ? other : ck;
+      ck = (desc == lower) ? hi_v : lo_v;
     }
-    return r;
-  };
-  const uint32_t kt = t < W ? okey[t] : 0u;
-  if (t < W) rank1[t] = count_beating(okey, kt);
+  }
+  const int spos = 255 - (int)(ck & 0xFFu);   // token at sorted index t (t < W)
+  if (t < W) rank1[spos] = t;
   __syncthreads();
   bool chunk = false;
   if (t < W) {
     for (int i = max(0, t - a.radius); i <= min(W - 1, t + a.radius); ++i) chunk |= rank1[i] < a.anchors;
-    okey2[t] = chunk ? 0u : kt;
+    kflag[t] = chunk ? 1 : 0;
   }
   const int nchunk = __syncthreads_count(t < W && chunk);
-  bool kept = chunk;
-  if (t < W && !chunk) kept = count_beating(okey2, kt) < K - nchunk;
+  // in sorted order: the first K - nchunk tokens outside the chunks
+  const bool sorted_free = t < W && kflag[spos] == 0;
+  const int before = block_excl_scan<kThreads>(sorted_free ? 1 : 0, tot2);
+  if (sorted_free && before < K - nchunk) kflag[spos] = 1;
+  __syncthreads();
+  const bool kept = t < W && kflag[t] != 0;
   // slot of each kept position: a workgroup scan of the flags
-  const int slot = block_excl_scan<kThreads>(t < W && kept ? 1 : 0, tot);
+  const int slot = block_excl_scan<kThreads>(kept ? 1 : 0, tot);
   int32_t* krow = a.keep_out + orow * K;
+  if (t < W) slot_of[t] = kept ? slot : -1;
   if (t < W && kept) {
     keep_s[slot] = t;
     krow[slot] = t0 + t;
   }
-  __syncthreads();
+  wait_vm<0>();      // this wave's V rows are in LDS (long done: they were its first loads)
+  __syncthreads();   // slots, and every wave's V rows
 
-  // compaction, K then V: slot t0 + i <- t0 + keep_s[i] for i < K.  The
-  // kept rows are copied HBM -> LDS (the ring, idle now) with
-  // global_load_lds, then written back from LDS: every row of a tensor is
-  // read before any is written (keep_s[i] >= i).  Wave w takes 64-piece
-  // groups w, w + 4, ...; lanes past the last piece load a kept row again
-  // into the unused tail of the buffer.
-  uint8_t* const stage = &ring[0][0][0];
-  const int pieces = K * PPR;
+  // compaction: row t0 + i <- row t0 + keep_s[i] for i < K, rows that move
+  // only.  K from the registers: wave w writes key blocks w, w + 4, ...
+  // (lane (col, g4) holds pieces 4 ks + g4 of key 16 j + col).  V from LDS.
+  uint8_t* const kbase = reinterpret_cast<uint8_t*>(a.k);
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    uint8_t* base = reinterpret_cast<uint8_t*>(x == 0 ? a.k : a.v);
-    for (int s0 = wave * kWave; s0 < pieces; s0 += kThreads) {
-      const int sp = s0 + lane, i = min(sp / PPR, K - 1), p = sp % PPR;
-      tile_piece_to_lds(base + rows.at(t0 + keep_s[i]) * 2 + p * 16, stage + s0 * 16);
+  for (int j = 0; j < NB; ++j) {
+    if (j % WAVES != wave) continue;
+    const int s = j * kBlockKeys + col, sl = slot_of[s];
+    if (sl >= 0 && sl != s) {
+      uint8_t* dst = kbase + rows.at(t0 + sl) * 2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<uint4*>(dst + (4 * ks + g4) * 16) = kf[j].w[ks];
     }
-    wait_vm<0>();
-    __syncthreads();
-    for (int sp = t; sp < pieces; sp += kThreads) {
-      const int i = sp / PPR, p = sp % PPR;
-      if (keep_s[i] != i)
-        *reinterpret_cast<uint4*>(base + rows.at(t0 + i) * 2 + p * 16) =
-            *reinterpret_cast<const uint4*>(stage + sp * 16);
-    }
-    __syncthreads();   // the buffer is read before the next tensor fills it
+  }
+  for (int sp = t; sp < K * PPR; sp += kThreads) {
+    const int i = sp / PPR, p = sp % PPR, src = keep_s[i];
+    if (src != i)
+      *reinterpret_cast<uint4*>(vbase + rows.at(t0 + i) * 2 + p * 16) =
+          *reinterpret_cast<const uint4*>(vwin + (src * PPR + p) * 16);
   }
 
   if (PAGED && a.free_blocks != nullptr && u.l == 0 && u.h == 0) {

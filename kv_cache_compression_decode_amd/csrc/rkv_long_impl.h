@@ -10,19 +10,24 @@
 // the C records in span order (so the C workgroups compute identical unit
 // statistics) and finishes its own keys' importance, redundancy and score.
 //
-// Units are launched P at a time (P * C workgroups: as many as are resident
-// on the device at once), unit unit0 + i taken by workgroups C*i .. C*i+C-1,
-// so the C workgroups a span waits for are all running.  Work of other kinds
-// on other streams can only delay some of them (it finishes and frees its
-// room); two such span launches at once on one device could hold each
-// other's room, which is why the interface asks for them on one stream.  The wait is a
-// spin on a per-unit counter (zeroed by a small kernel first), bounded (one
-// second unless the caller sets another bound) so that no launch can hang
-// the device; it is never reached when the launch's workgroups are
-// dispatched.  A span whose wait reaches the bound sets kSpanTimeout in the
-// call's status word and finishes with wrong scores; the selection and
-// compaction kernels of the call then leave the keep rows and the cache
-// untouched.
+// One launch takes every unit.  A workgroup's span is given by a ticket it
+// draws when it starts (an atomic counter): consecutive tickets are the
+// spans of one unit, in unit order.  A span therefore only waits for spans that
+// started before it or that the next starting workgroups will take: while
+// a unit's spans are not all running, every other running workgroup belongs
+// to a unit whose spans all are, so it finishes and frees room for the next
+// ticket (this needs room for a unit's workgroups on the device, which the
+// launch checks).  Units start one after another as room frees.  Work of
+// other kinds on other streams can only delay some of them (it finishes and
+// frees its room); two such span launches at once on one device could hold
+// each other's room, which is why the interface asks for them on one
+// stream.  The wait is a spin on a per-unit counter (zeroed, with the ticket
+// counter, by a small kernel first), bounded (one second unless the caller
+// sets another bound) so that no launch can hang the device; it is never
+// reached when the launch's workgroups are dispatched.  A span whose wait
+// reaches the bound sets kSpanTimeout in the call's status word and
+// finishes with wrong scores; the selection and compaction kernels of the
+// call then leave the keep rows and the cache untouched.
 #pragma once
 
 #include <algorithm>
@@ -35,7 +40,6 @@ namespace rkv {
 struct LongArgs {
   int64_t wait_ticks;   // bound on the wait for the other spans (s_memrealtime, 100 MHz)
   int32_t chunks;       // C: workgroups (key spans) per unit
-  int32_t unit0;        // first unit of this launch: workgroup w takes span w % C of unit0 + w / C
 };
 
 // Counter of unit ui: the first word of record slot C of the unit (the
@@ -44,9 +48,16 @@ __device__ __forceinline__ uint32_t* long_counter(const ScoreArgs& a, int ui, in
   return reinterpret_cast<uint32_t*>(a.part + ((size_t)ui * a.max_chunks + C) * a.rec);
 }
 
+// Ticket counter of a launch: word 32 of unit 0's counter slot (a record
+// slot holds 2 G w + D >= 66 words), on its own 128-byte line.
+__device__ __forceinline__ uint32_t* long_tickets(const ScoreArgs& a, int C) {
+  return long_counter(a, 0, C) + 32;
+}
+
 static __global__ void long_zero_kernel(ScoreArgs a, int C, int units) {
   const int ui = blockIdx.x * blockDim.x + threadIdx.x;
   if (ui < units) *long_counter(a, ui, C) = 0u;
+  if (ui == 0) *long_tickets(a, C) = 0u;
   if (a.reset_status) clear_status_first(a.status);
 }
 
@@ -118,15 +129,19 @@ __device__ __forceinline__ void merge_span_stats(UnitLds<D, RT>& L, const float*
 template <bool PAGED, int D, int RT>
 __global__ __launch_bounds__(kUnitThreads) void score_long_kernel(ScoreArgs a, LongArgs la) {
   __shared__ UnitLds<D, RT> L;
+  __shared__ uint32_t ticket;
   KeyFrag<true, D> kf[UnitShape<D>::NBW];
-  const int C = la.chunks;
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
-  const int c = blockIdx.x % C, t = threadIdx.x, gw = a.gw;
+  const int t = threadIdx.x, gw = a.gw;
   // a bad block id (set before this launch, so every span reads the same
   // value): the pool must not be read
   if (a.check_blocks && step_aborted(a.status, kBadBlockId)) return;
+  const int C = la.chunks;
+  if (t == 0) ticket = __hip_atomic_fetch_add(long_tickets(a, C), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int c = (int)(ticket % (uint32_t)C);
   {
-    const int ui = la.unit0 + blockIdx.x / C;
+    const int ui = (int)(ticket / (uint32_t)C);
     if (ui >= units) return;
     const Unit u = decode_unit(a.g, a.tt, ui);
     if (u.n == 0) return;   // past the device table's count: all C workgroups skip it
@@ -171,18 +186,14 @@ hipError_t launch_long_t(const ScoreArgs& a, int chunks, hipStream_t st) {
     resident = cus * occ;
     grid_of[dev].store(resident, std::memory_order_relaxed);
   }
-  const int per = resident / chunks;   // units whose spans are all resident at once
-  if (per < 1) return hipErrorInvalidConfiguration;
+  if (resident < chunks) return hipErrorInvalidConfiguration;   // a unit's spans must fit at once
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
   hipLaunchKernelGGL(long_zero_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a, chunks, units);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int u0 = 0; u0 < units; u0 += per) {
-    LongArgs la{span_wait_ticks(), chunks, u0};   // default 1 s: far beyond any wait of a resident launch
-    const int grid = std::min(per, units - u0) * chunks;
-    hipLaunchKernelGGL((score_long_kernel<PAGED, D, RT>), dim3(grid), dim3(kUnitThreads), 0, st, a, la);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  LongArgs la{span_wait_ticks(), chunks};   // default 1 s: far beyond any wait of a dispatched span
+  hipLaunchKernelGGL((score_long_kernel<PAGED, D, RT>), dim3(units * chunks), dim3(kUnitThreads), 0, st, a,
+                     la);
+  return hipGetLastError();
 }
 
 template <bool PAGED, int D>
