@@ -13,8 +13,10 @@
 // both are in flight together.  The keep row is staged in LDS first, and
 // the walk starts at the first slot that moves (keep[i] == i below it).
 //
-// One workgroup per (unit, K or V, column part); each row slice is read by
-// consecutive lanes, 16 bytes per lane.
+// One workgroup per (unit, K or V); each row is read by consecutive lanes,
+// 16 bytes per lane.  (Splitting the rows into column parts over more
+// workgroups measured slower: whole rows per workgroup give the longest
+// contiguous accesses.)
 #include "rkv_device.h"
 #include "rkv_launch.h"
 
@@ -37,7 +39,7 @@ __device__ __forceinline__ int64_t row_at(const CompactArgs& a, const Unit& u, i
 
 }  // namespace
 
-// TPR: threads per row slice (slice bytes / 16); PARTS: column parts per row
+// TPR: threads per row (row bytes / 16); PARTS: column parts per row
 template <bool PAGED, int TPR, int PARTS>
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   constexpr int R = kCompactRows;
@@ -104,12 +106,12 @@ static hipError_t prepare_compact() {
   static hipError_t once = [] {
     const int lds = RKV_MAX_LEN * (int)sizeof(int32_t);
     hipError_t e = hipSuccess;
-    const void* fns[] = {reinterpret_cast<const void*>(compact_kernel<false, 4, 2>),
-                         reinterpret_cast<const void*>(compact_kernel<false, 8, 2>),
-                         reinterpret_cast<const void*>(compact_kernel<false, 16, 2>),
-                         reinterpret_cast<const void*>(compact_kernel<true, 4, 2>),
-                         reinterpret_cast<const void*>(compact_kernel<true, 8, 2>),
-                         reinterpret_cast<const void*>(compact_kernel<true, 16, 2>)};
+    const void* fns[] = {reinterpret_cast<const void*>(compact_kernel<false, 8, 1>),
+                         reinterpret_cast<const void*>(compact_kernel<false, 16, 1>),
+                         reinterpret_cast<const void*>(compact_kernel<false, 32, 1>),
+                         reinterpret_cast<const void*>(compact_kernel<true, 8, 1>),
+                         reinterpret_cast<const void*>(compact_kernel<true, 16, 1>),
+                         reinterpret_cast<const void*>(compact_kernel<true, 32, 1>)};
     for (const void* f : fns) {
       hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (r != hipSuccess) e = r;
@@ -122,27 +124,27 @@ static hipError_t prepare_compact() {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t st) {
   const int units = a.g.num_trig * a.g.num_layers * a.g.hkv;
   if (units == 0) return hipSuccess;
-  const dim3 grid(units * 2 * 2);
+  const dim3 grid(units * 2);
   const size_t lds = (size_t)a.g.budget * sizeof(int32_t);
   if (lds > 48 * 1024) {
     const hipError_t e = prepare_compact();
     if (e != hipSuccess) return e;
   }
-  // rows split in two column halves: 64, 128 or 256 bytes per workgroup row
+  // whole rows of 128, 256 or 512 bytes per workgroup
   const dim3 blk(kThreads);
-#define RKV_COMPACT(P, T) hipLaunchKernelGGL((compact_kernel<P, T, 2>), grid, blk, lds, st, a)
+#define RKV_COMPACT(P, T) hipLaunchKernelGGL((compact_kernel<P, T, 1>), grid, blk, lds, st, a)
   if (a.g.paged) {
     switch (a.row_bytes) {
-      case 128: RKV_COMPACT(true, 4); break;
-      case 256: RKV_COMPACT(true, 8); break;
-      case 512: RKV_COMPACT(true, 16); break;
+      case 128: RKV_COMPACT(true, 8); break;
+      case 256: RKV_COMPACT(true, 16); break;
+      case 512: RKV_COMPACT(true, 32); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (a.row_bytes) {
-      case 128: RKV_COMPACT(false, 4); break;
-      case 256: RKV_COMPACT(false, 8); break;
-      case 512: RKV_COMPACT(false, 16); break;
+      case 128: RKV_COMPACT(false, 8); break;
+      case 256: RKV_COMPACT(false, 16); break;
+      case 512: RKV_COMPACT(false, 32); break;
       default: return hipErrorInvalidValue;
     }
   }
