@@ -13,17 +13,19 @@
 // both are in flight together.  The keep row is staged in LDS first, and
 // the walk starts at the first slot that moves (keep[i] == i below it).
 //
-// One workgroup per (unit, K or V); each row is read by consecutive lanes,
-// 16 bytes per lane.  (Splitting the rows into column parts over more
-// workgroups measured slower: whole rows per workgroup give the longest
-// contiguous accesses.)
+// One 1024-thread workgroup per (unit, K or V); each row is read by
+// consecutive lanes, 16 bytes per lane.  (Splitting the rows into column
+// parts over more workgroups measured slower: whole rows per workgroup give
+// the longest contiguous accesses; 1024 threads keep 128 KB of rows in
+// flight per workgroup, which the batches of few units need.)
 #include "rkv_device.h"
 #include "rkv_launch.h"
 
 namespace rkv {
 
 namespace {
-constexpr int kCompactRows = 8;   // rows per thread per tile (named registers below)
+constexpr int kCompactRows = 8;        // rows per thread per tile (named registers below)
+constexpr int kCompactThreads = 1024;  // per workgroup: 64 rows of 256 bytes per pass
 
 // Element offset of token t's row; base = head_base of the unit.
 template <bool PAGED>
@@ -39,18 +41,17 @@ __device__ __forceinline__ int64_t row_at(const CompactArgs& a, const Unit& u, i
 
 }  // namespace
 
-// TPR: threads per row (row bytes / 16); PARTS: column parts per row
-template <bool PAGED, int TPR, int PARTS>
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
-  constexpr int R = kCompactRows;
-  constexpr int RPP = kThreads / TPR;   // rows per pass
+// TPR: threads per row (row bytes / 16)
+template <bool PAGED, int TPR>
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
+  constexpr int NT = kCompactThreads, R = kCompactRows;
+  constexpr int RPP = NT / TPR;         // rows per pass
   constexpr int TILE = RPP * R;         // rows per read/write round
   extern __shared__ int32_t keep_s[];
   __shared__ int first_moved;
 
-  const int part = blockIdx.x % PARTS;
-  const int which = (blockIdx.x / PARTS) & 1;
-  const int unit_id = blockIdx.x / (2 * PARTS);
+  const int which = blockIdx.x & 1;
+  const int unit_id = blockIdx.x / 2;
   const Unit u = decode_unit(a.g, a.tt, unit_id);
   if (u.n == 0) return;   // past the device table's count
   if (step_aborted(a.status)) return;   // the step failed a device check: cache untouched
@@ -58,15 +59,14 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int64_t hb = head_base(a.g, u.l, u.s, u.h);
   const int budget = a.g.budget;
   const int esize = a.row_bytes / a.g.d;
-  uint8_t* base = reinterpret_cast<uint8_t*>(which ? a.v : a.k) + part * (TPR * 16) +
-                  (tid % TPR) * 16;
+  uint8_t* base = reinterpret_cast<uint8_t*>(which ? a.v : a.k) + (tid % TPR) * 16;
   const int rr = tid / TPR;
   const int32_t* krow = a.keep + out_row(a.g, u) * budget;
 
   if (tid == 0) first_moved = budget;
   __syncthreads();
   int lo = budget;
-  for (int i = tid; i < budget; i += kThreads) {
+  for (int i = tid; i < budget; i += NT) {
     const int src = krow[i];
     keep_s[i] = src;
     if (src != i) lo = min(lo, i);
@@ -84,6 +84,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     const uint4 b##r = stream_load(reinterpret_cast<const uint4*>(                   \
         base + row_at<PAGED>(a, u, hb, keep_s[s##r]) * esize));
 #define RKV_STORE(r) stream_store(reinterpret_cast<uint4*>(base + row_at<PAGED>(a, u, hb, s##r) * esize), b##r);
+    static_assert(R == 8, "eight named row registers");
     RKV_LOAD(0) RKV_LOAD(1) RKV_LOAD(2) RKV_LOAD(3) RKV_LOAD(4) RKV_LOAD(5) RKV_LOAD(6) RKV_LOAD(7)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -93,32 +94,25 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
 #undef RKV_STORE
   }
 
-  if (a.free_blocks != nullptr && which == 0 && part == 0 && u.l == 0 && u.h == 0) {
+  if (a.free_blocks != nullptr && which == 0 && u.l == 0 && u.h == 0) {
     const int bs = 1 << a.g.bs_shift;
     const int first = (budget + bs - 1) / bs, last = (u.n + bs - 1) / bs;
     int32_t* out = a.free_blocks + free_off(a.g, a.tt, u.ti);
-    for (int b = first + tid; b < last; b += kThreads)
+    for (int b = first + tid; b < last; b += NT)
       out[b - first] = a.bt[(int64_t)u.s * a.g.maxblk + b];
   }
 }
 
-static hipError_t prepare_compact() {
-  static hipError_t once = [] {
-    const int lds = RKV_MAX_LEN * (int)sizeof(int32_t);
-    hipError_t e = hipSuccess;
-    const void* fns[] = {reinterpret_cast<const void*>(compact_kernel<false, 8, 1>),
-                         reinterpret_cast<const void*>(compact_kernel<false, 16, 1>),
-                         reinterpret_cast<const void*>(compact_kernel<false, 32, 1>),
-                         reinterpret_cast<const void*>(compact_kernel<true, 8, 1>),
-                         reinterpret_cast<const void*>(compact_kernel<true, 16, 1>),
-                         reinterpret_cast<const void*>(compact_kernel<true, 32, 1>)};
-    for (const void* f : fns) {
-      hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (r != hipSuccess) e = r;
-    }
-    return e;
-  }();
-  return once;
+template <bool PAGED, int TPR>
+hipError_t launch_compact_t(const CompactArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (lds > 48 * 1024) {
+    static const hipError_t once = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(compact_kernel<PAGED, TPR>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, RKV_MAX_LEN * (int)sizeof(int32_t));
+    if (once != hipSuccess) return once;
+  }
+  hipLaunchKernelGGL((compact_kernel<PAGED, TPR>), grid, dim3(kCompactThreads), lds, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t st) {
@@ -126,30 +120,13 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t st) {
   if (units == 0) return hipSuccess;
   const dim3 grid(units * 2);
   const size_t lds = (size_t)a.g.budget * sizeof(int32_t);
-  if (lds > 48 * 1024) {
-    const hipError_t e = prepare_compact();
-    if (e != hipSuccess) return e;
-  }
   // whole rows of 128, 256 or 512 bytes per workgroup
-  const dim3 blk(kThreads);
-#define RKV_COMPACT(P, T) hipLaunchKernelGGL((compact_kernel<P, T, 1>), grid, blk, lds, st, a)
-  if (a.g.paged) {
-    switch (a.row_bytes) {
-      case 128: RKV_COMPACT(true, 8); break;
-      case 256: RKV_COMPACT(true, 16); break;
-      case 512: RKV_COMPACT(true, 32); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (a.row_bytes) {
-      case 128: RKV_COMPACT(false, 8); break;
-      case 256: RKV_COMPACT(false, 16); break;
-      case 512: RKV_COMPACT(false, 32); break;
-      default: return hipErrorInvalidValue;
-    }
+  switch (a.row_bytes) {
+    case 128: return a.g.paged ? launch_compact_t<true, 8>(a, grid, lds, st) : launch_compact_t<false, 8>(a, grid, lds, st);
+    case 256: return a.g.paged ? launch_compact_t<true, 16>(a, grid, lds, st) : launch_compact_t<false, 16>(a, grid, lds, st);
+    case 512: return a.g.paged ? launch_compact_t<true, 32>(a, grid, lds, st) : launch_compact_t<false, 32>(a, grid, lds, st);
+    default: return hipErrorInvalidValue;
   }
-#undef RKV_COMPACT
-  return hipGetLastError();
 }
 
 }  // namespace rkv
