@@ -27,10 +27,11 @@ def shape_cfg(spec):
                          spec.layout, spec.block_size)
 
 
-def run_kara(case, kc, tails, workspace=None):
+def run_kara(case, kc, tails, workspace=None, q_host=None):
     spec = case.spec
     W, K = kc.window_len, kc.keep
-    q_host = syn.build_queries(spec.with_(window=W))
+    if q_host is None:
+        q_host = syn.build_queries(spec.with_(window=W))
     q = to_dev(q_host)
     rows = spec.num_layers * spec.num_seqs * spec.num_kv_heads
     scores = torch.full((rows * W,), float("nan"), device="cuda")
@@ -202,6 +203,50 @@ def test_kara_llama8b_full_batch():
     res = run_kara(case, B.rkv_kara_config(128, 32, 4, 2), (1024,))
     ties = check(case, kc, (1024,), res, before=contig_before_from_host(case))
     log(f"kara full batch: {ties} of 256 units decided by an oracle near-tie")
+
+
+@pytest.mark.parametrize("mode", ["zero-queries", "two-key-values"])
+def test_kara_exact_ties(mode):
+    """Scores that tie exactly, where only the position order decides.
+    zero-queries: every window token gets weight 1/W from every row, so all
+    scores are equal and the rule keeps the window's first `keep` tokens (a
+    reversed tie order would keep the last ones).  two-key-values: the window
+    keys alternate between two vectors, so the scores take two values and
+    each group is ranked by position; the anchors' chunks then make rows
+    move.  Both against the oracle, whose float64 scores tie the same way."""
+    spec = syn.config(1).with_(name=f"kara-ties-{mode}", seed=78, num_seqs=2, num_layers=2,
+                               num_q_heads=8, num_kv_heads=2, lens=(400, 300))
+    kc = SimpleNamespace(window_len=64, keep=20, anchors=2, radius=3)
+    W, tails = kc.window_len, (336, 236)
+    case = ContigCase(spec)
+    q_host = None
+    if mode == "zero-queries":
+        q_host = np.zeros_like(syn.build_queries(spec.with_(window=W)))
+    else:
+        for s in range(spec.num_seqs):
+            t0 = int(case.lens0[s]) - W
+            win = case.k_host[:, s, :, t0:t0 + W]
+            win[:, :, 0::2] = win[:, :, :1].copy()
+            win[:, :, 1::2] = win[:, :, 1:2].copy()
+        case.k.copy_(to_dev(case.k_host))
+    before = {(s, l, h): (case.unit_rows(s, l, h)[0].copy(), case.unit_rows(s, l, h)[1].copy())
+              for s in range(spec.num_seqs) for l in range(spec.num_layers)
+              for h in range(spec.num_kv_heads)}
+    res = run_kara(case, B.rkv_kara_config(W, kc.keep, kc.anchors, kc.radius), tails, q_host=q_host)
+    ties = check(case, kc, tails, res, before=lambda s, l, h: before[(s, l, h)])
+    assert ties == 0, "exact ties are decided by position on both sides"
+    if mode == "zero-queries":
+        for s in range(spec.num_seqs):
+            t0 = int(case.lens0[s]) - W
+            for l in range(spec.num_layers):
+                for h in range(spec.num_kv_heads):
+                    row = (l * spec.num_seqs + s) * spec.num_kv_heads + h
+                    assert np.all(res.scores[row] == res.scores[row][0])
+                    assert np.array_equal(res.keep[row], t0 + np.arange(kc.keep))
+    else:
+        moved = sum(int((res.keep[r] != res.keep[r][0] + np.arange(kc.keep)).any())
+                    for r in range(res.keep.shape[0]))
+        assert moved > 0, "the two-valued scores should make some kept rows move"
 
 
 def contig_before_from_host(case):
