@@ -61,15 +61,19 @@ static __global__ void long_zero_kernel(ScoreArgs a, int C, int units) {
   if (a.reset_status) clear_status_first(a.status);
 }
 
-// Every thread's earlier global stores are published, then this workgroup
-// adds one to the unit's counter and waits until it reaches target (or the
-// time bound passes: then kSpanTimeout goes into the status word; a bound of
-// 0 gives up at once and always reports it).  All threads call it.
+// The workgroup's record stores (agent-scope atomic stores: written through
+// to the device's coherence point) have completed, then this workgroup adds
+// one to the unit's counter and waits until it reaches target (or the time
+// bound passes: then kSpanTimeout goes into the status word; a bound of 0
+// gives up at once and always reports it).  All threads call it.  The
+// records are read back with agent-scope atomic loads, so neither side
+// writes back or invalidates the XCD's L2 (an agent-scope fence would do
+// both, for every span).
 __device__ __forceinline__ void span_signal_wait(uint32_t* cnt, uint32_t target, int64_t wait_ticks,
                                                  uint32_t* status) {
-  __syncthreads();   // every store of the workgroup performed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's record stores are done
+  __syncthreads();                                    // ... and every other thread's
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
     bool done = false;
@@ -82,9 +86,15 @@ __device__ __forceinline__ void span_signal_wait(uint32_t* cnt, uint32_t target,
     }
     if (!done && status != nullptr)
       __hip_atomic_fetch_or(status, kSpanTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void rec_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float rec_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The span's record (row max, raw sum, direction sum) into slot c of the
@@ -96,10 +106,10 @@ __device__ __forceinline__ void publish_span_stats(UnitLds<D, RT>& L, float* rec
   const int t = threadIdx.x;
   float* mine = recs + (size_t)c * rec;
   if (t < gw) {
-    mine[t] = empty ? -INFINITY : L.row_m[t];
-    mine[gw + t] = empty ? 0.f : L.row_iz[t];
+    rec_store(mine + t, empty ? -INFINITY : L.row_m[t]);
+    rec_store(mine + gw + t, empty ? 0.f : L.row_iz[t]);
   }
-  if (t < D) mine[2 * gw + t] = empty ? 0.f : L.red_s[t][0];
+  if (t < D) rec_store(mine + 2 * gw + t, empty ? 0.f : L.red_s[t][0]);
 }
 
 // The unit's row statistics and direction-sum rows from the C records,
@@ -113,13 +123,13 @@ __device__ __forceinline__ void merge_span_stats(UnitLds<D, RT>& L, const float*
     float mm = -INFINITY, zz = 0.f;
     if (t < gw)
       for (int cc = 0; cc < C; ++cc)
-        merge_stats(mm, zz, recs[(size_t)cc * rec + t], recs[(size_t)cc * rec + gw + t]);
+        merge_stats(mm, zz, rec_load(recs + (size_t)cc * rec + t), rec_load(recs + (size_t)cc * rec + gw + t));
     L.row_m[t] = t < gw ? mm : INFINITY;   // log2 units; other rows add nothing
     L.row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
   }
   if (t < D) {   // the unit's sum of khat, split into the two bf16 rows gw and gw + 1
     float sv = 0.f;
-    for (int cc = 0; cc < C; ++cc) sv += recs[(size_t)cc * rec + 2 * gw + t];
+    for (int cc = 0; cc < C; ++cc) sv += rec_load(recs + (size_t)cc * rec + 2 * gw + t);
     const uint32_t hi = f2bf_bits(sv);
     L.q[gw * QP + t] = (uint16_t)hi;
     L.q[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
