@@ -29,10 +29,12 @@
  *   - bf16 units longer than one workgroup holds (more than 1280 keys at
  *     head_dim 128, 2560 at 64) are scored by several workgroups that wait
  *     for one another (rkv_score, and rkv_step / rkv_step_device when they
- *     fall back to the three kernels).  Each launch only takes as many
- *     workgroups as the device holds at once, but two such launches running
- *     at the same time on different streams of one device can hold each
- *     other's room: run such calls on one stream (or one at a time).  The
+ *     fall back to the three kernels).  A workgroup takes its span from a
+ *     ticket it draws when it starts, so a span only waits for spans that
+ *     started before it or that the next starting workgroups take, and one
+ *     such launch always completes; two of them running at the same time on
+ *     different streams of one device can hold each other's room: run such
+ *     calls on one stream (or one at a time).  The
  *     wait is bounded (one second by default, rkv_set_span_wait_us), so the
  *     device never hangs.  A wait that reaches the bound sets
  *     RKV_DEVICE_SPAN_TIMEOUT in the workspace's status word; selection and
