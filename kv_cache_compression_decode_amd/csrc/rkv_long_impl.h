@@ -113,7 +113,12 @@ __device__ __forceinline__ void publish_span_stats(UnitLds<D, RT>& L, float* rec
 }
 
 // The unit's row statistics and direction-sum rows from the C records,
-// merged in span order (every span computes the same values).
+// merged in span order (every span computes the same values).  The records
+// are read kRecBatch spans at a time, each batch's loads issued together:
+// they come from the coherence point, so one at a time would pay its
+// latency C times.
+constexpr int kRecBatch = 4;
+
 template <int D, int RT>
 __device__ __forceinline__ void merge_span_stats(UnitLds<D, RT>& L, const float* recs, int rec, int C,
                                                  int gw) {
@@ -122,14 +127,32 @@ __device__ __forceinline__ void merge_span_stats(UnitLds<D, RT>& L, const float*
   if (t < RT * 16) {
     float mm = -INFINITY, zz = 0.f;
     if (t < gw)
-      for (int cc = 0; cc < C; ++cc)
-        merge_stats(mm, zz, rec_load(recs + (size_t)cc * rec + t), rec_load(recs + (size_t)cc * rec + gw + t));
+      for (int c0 = 0; c0 < C; c0 += kRecBatch) {
+        float m4[kRecBatch], z4[kRecBatch];
+#pragma unroll
+        for (int i = 0; i < kRecBatch; ++i) {
+          const size_t cc = (size_t)min(c0 + i, C - 1);
+          m4[i] = rec_load(recs + cc * rec + t);
+          z4[i] = rec_load(recs + cc * rec + gw + t);
+        }
+#pragma unroll
+        for (int i = 0; i < kRecBatch; ++i)
+          if (c0 + i < C) merge_stats(mm, zz, m4[i], z4[i]);
+      }
     L.row_m[t] = t < gw ? mm : INFINITY;   // log2 units; other rows add nothing
     L.row_iz[t] = t < gw ? 1.f / (zz * (float)gw) : 0.f;
   }
   if (t < D) {   // the unit's sum of khat, split into the two bf16 rows gw and gw + 1
     float sv = 0.f;
-    for (int cc = 0; cc < C; ++cc) sv += rec_load(recs + (size_t)cc * rec + 2 * gw + t);
+    for (int c0 = 0; c0 < C; c0 += kRecBatch) {
+      float s4[kRecBatch];
+#pragma unroll
+      for (int i = 0; i < kRecBatch; ++i)
+        s4[i] = rec_load(recs + (size_t)min(c0 + i, C - 1) * rec + 2 * gw + t);
+#pragma unroll
+      for (int i = 0; i < kRecBatch; ++i)
+        if (c0 + i < C) sv += s4[i];
+    }
     const uint32_t hi = f2bf_bits(sv);
     L.q[gw * QP + t] = (uint16_t)hi;
     L.q[(gw + 1) * QP + t] = (uint16_t)f2bf_bits(sv - __uint_as_float(hi << 16));
