@@ -156,4 +156,47 @@ def pin_step_unit_gqa_and_window(k):
     assert np.array_equal(res["v_new"], vrows[n - w:][want])
 
 
+def _bf16_bits(x):
+    """bf16 storage of float32 values that bf16 holds exactly (a bf16 is the
+    upper half of an IEEE binary32)."""
+    x = np.asarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    assert np.all(bits & np.uint32(0xFFFF) == 0), "value not exact in bf16"
+    return (bits >> np.uint32(16)).astype(np.uint16)
+
+
+def pin_decode_bf16_patterns(k):
+    """bf16 widening against hand-decoded bit patterns: sign, exponent bias
+    127, 7 stored fraction bits, subnormals, infinities."""
+    pats = [0x3F80, 0xBF80, 0x4040, 0x3F81, 0xC2F7, 0x0000, 0x8000, 0x0001, 0x7F80, 0xFF80, 0x0080]
+    want = [1.0, -1.0, 3.0, 1.0 + 2.0 ** -7, -123.5, 0.0, -0.0, 2.0 ** -133, math.inf, -math.inf,
+            2.0 ** -126]
+    got = k._decode(np.array(pats, dtype=np.uint16), "bf16")
+    assert got.dtype == np.float64
+    for g, w_, p in zip(got, want, pats):
+        assert g == w_ and math.copysign(1.0, g) == math.copysign(1.0, w_), (hex(p), g, w_)
+
+
+def pin_step_unit_bf16(k):
+    """step_unit on bf16 storage: scores from the widened values, kept rows
+    returned as the stored bit patterns (here G = 2, h = 0)."""
+    from types import SimpleNamespace
+    rng = np.random.default_rng([78, 61])
+    hq, hkv, w, d, n = 4, 2, 8, 4, 13
+    kc = SimpleNamespace(window_len=w, keep=4, anchors=1, radius=1)
+    # small multiples of 1/8: exact in bf16
+    q = (rng.integers(-16, 17, (hq, w, d)) / 8.0).astype(np.float32)
+    krows = (rng.integers(-16, 17, (n, d)) / 8.0).astype(np.float32)
+    vrows = (rng.integers(-16, 17, (n, d)) / 8.0).astype(np.float32)
+    qb, kb, vb = _bf16_bits(q), _bf16_bits(krows), _bf16_bits(vrows)
+    res = k.step_unit(kc, "bf16", hq, hkv, qb, kb, vb, 0)
+    rows = np.concatenate([q[0], q[1]]).astype(np.float64)
+    s = brute.kara_scores(rows.tolist(), krows[n - w:].astype(np.float64).tolist())
+    _close(res["score"], s)
+    want = brute.kara_keep(s, 4, 1, 1)
+    assert list(res["keep"]) == want
+    assert res["k_new"].dtype == np.uint16 and np.array_equal(res["k_new"], kb[n - w:][want])
+    assert res["v_new"].dtype == np.uint16 and np.array_equal(res["v_new"], vb[n - w:][want])
+
+
 ALL_PINS = [v for kk, v in sorted(globals().items()) if kk.startswith("pin_")]

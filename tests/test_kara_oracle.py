@@ -44,6 +44,16 @@ MUTANTS = [
     ("window taken from the front", "kw, vw = k_rows[n - w:n], v_rows[n - w:n]", "kw, vw = k_rows[:w], v_rows[:w]"),
     ("GQA group ignored", "q = q_group_window(_decode(q_tail_sl, dtype), h, group)",
      "q = q_group_window(_decode(q_tail_sl, dtype), h, 1)"),
+    ("bf16 decode without the 16-bit shift", "astype(np.uint32) << np.uint32(16)",
+     "astype(np.uint32) << np.uint32(8)"),
+    ("bf16 decode drops the sign", "w = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
+     "w = (np.asarray(x, dtype=np.uint16).astype(np.uint32) & np.uint32(0x7FFF)) << np.uint32(16)"),
+    ("bf16 decode with swapped bytes", "w = np.asarray(x, dtype=np.uint16).astype",
+     "w = np.asarray(x, dtype=np.uint16).byteswap().astype"),
+    ("f32 decode through half precision", "return np.asarray(x, dtype=np.float32).astype(np.float64)",
+     "return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)"),
+    ("step_unit returns widened rows", "return unit_step(q, _decode(kw, dtype), kw, vw,",
+     "return unit_step(q, _decode(kw, dtype), _decode(kw, dtype), vw,"),
 ]
 
 
