@@ -17,7 +17,8 @@
 //
 // One 256-thread workgroup per unit does all three steps.  Every wave holds
 // the W window keys in registers as MFMA operands (keys x rows products, as
-// in the R-KV scoring) and takes every fourth 16-row tile of the query rows,
+// in the R-KV scoring; read from one copy in LDS that the workgroup loads
+// once) and takes every fourth 16-row tile of the query rows,
 // so each query row is read from HBM once.  A tile's row
 // softmax needs no other wave (its wave holds every key); the per-key sums
 // of the weights stay in registers until the end, then one DPP row sum and
@@ -67,8 +68,15 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   constexpr int VI = W * PPR / kThreads;              // wave-wide 16-byte loads per wave for the V rows
   static_assert(W <= kKaraMaxW, "window");
   static_assert(VI >= 1 && VI * kThreads == W * PPR, "V rows in whole wave-wide loads");
+  // The window's K rows go through LDS (once per workgroup) unless that
+  // would cost the CU its second workgroup (LDS bytes: ring, V rows, K rows,
+  // and the small arrays below); else every wave loads them itself.
+  constexpr int kRowsLds = W * PPR * 16;
+  constexpr int kOtherLds = WAVES * kRing * TILE_BYTES + kRowsLds + 44 * W + 8 * WAVES;
+  constexpr bool KLDS = kOtherLds + kRowsLds <= 80 * 1024 || kOtherLds > 80 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][kRing][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vwin[W * PPR * 16];   // the window's V rows
+  __shared__ __attribute__((aligned(16))) uint8_t kwin[KLDS ? kRowsLds : 16];   // its K rows (swizzled)
   __shared__ float part[WAVES][W];
   __shared__ __attribute__((aligned(16))) uint32_t okey[W];
   __shared__ uint64_t xchg[W];   // bitonic exchange across the two waves
@@ -95,10 +103,23 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
     const int s0 = (wave * VI + i) * kWave, sp = s0 + lane;
     tile_piece_to_lds(vbase + rows.at(t0 + sp / PPR) * 2 + (sp % PPR) * 16, vwin + s0 * 16);
   }
-  // the W window keys: block j holds key j*16 + col, dims 32 ks + 8 g4 .. +7
+  // the window's K rows into LDS once per workgroup (every wave needs all of
+  // them; loading them per wave spends the CU's load bandwidth four times):
+  // piece p of row r at position r * PPR + (p ^ (r % PPR)), so that the
+  // fragment reads below fall on different banks; next-oldest loads.  (Without
+  // room for that copy, each wave loads the keys into its registers.)
+  const uint8_t* const ksrc = reinterpret_cast<const uint8_t*>(a.k);
   KeyFrag<true, D> kf[NB];
+  if constexpr (KLDS) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) kf[j].load(a.k, rows.at(t0 + j * kBlockKeys + col), g4, true);
+    for (int i = 0; i < VI; ++i) {
+      const int s0 = (wave * VI + i) * kWave, sp = s0 + lane, r = sp / PPR, p = (sp % PPR) ^ (r % PPR);
+      tile_piece_to_lds(ksrc + rows.at(t0 + r) * 2 + p * 16, kwin + s0 * 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) kf[j].load(a.k, rows.at(t0 + j * kBlockKeys + col), g4, true);
+  }
 
   // The unit's query rows, 16-row tiles; wave w takes tiles w, w + 4, ...,
   // each copied into the wave's ring of kRing tile slots, kRing - 1 tiles
@@ -121,6 +142,27 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   for (int k = 0; k < kRing - 1; ++k)
     if (k < my_tiles) issue(k);
 
+  // V and K rows in LDS (the first tiles may still be in flight), for every
+  // wave; then the W window keys as MFMA operands: block j holds key
+  // j*16 + col, dims 32 ks + 8 g4 .. +7
+  static_assert(kRing == 4, "the waits count up to three tiles in flight");
+  if constexpr (KLDS) {
+    switch (min(my_tiles, kRing - 1)) {
+      case 3: wait_vm<3 * NI>(); break;
+      case 2: wait_vm<2 * NI>(); break;
+      case 1: wait_vm<NI>(); break;
+      default: wait_vm<0>(); break;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = j * kBlockKeys + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[j].w[ks] = *reinterpret_cast<const uint4*>(kwin + (r * PPR + ((4 * ks + g4) ^ (r % PPR))) * 16);
+    }
+  }
+
   float acc[NB][4];
 #pragma unroll
   for (int j = 0; j < NB; ++j)
@@ -130,7 +172,6 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
     // tile k's loads are done once only the tiles issued after it are in
     // flight (min(my_tiles - 1 - k, kRing - 1) of them)
     if (k + kRing - 1 < my_tiles) issue(k + kRing - 1);
-    static_assert(kRing == 4, "the waits below count up to three tiles in flight");
     switch (min(my_tiles - 1 - k, kRing - 1)) {
       case 3: wait_vm<3 * NI>(); break;
       case 2: wait_vm<2 * NI>(); break;
