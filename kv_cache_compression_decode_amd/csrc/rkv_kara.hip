@@ -95,19 +95,12 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
 
   KeyRows<PAGED> rows;
   rows.init(a.g, a.bt, u);
-  // the window's V rows into LDS (piece p of row r at r * PPR + p); these are
-  // the oldest loads of every wave, so each wait below also covers them
-  uint8_t* const vbase = reinterpret_cast<uint8_t*>(a.v);
-#pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int s0 = (wave * VI + i) * kWave, sp = s0 + lane;
-    tile_piece_to_lds(vbase + rows.at(t0 + sp / PPR) * 2 + (sp % PPR) * 16, vwin + s0 * 16);
-  }
   // the window's K rows into LDS once per workgroup (every wave needs all of
   // them; loading them per wave spends the CU's load bandwidth four times):
   // piece p of row r at position r * PPR + (p ^ (r % PPR)), so that the
-  // fragment reads below fall on different banks; next-oldest loads.  (Without
-  // room for that copy, each wave loads the keys into its registers.)
+  // fragment reads below fall on different banks; the oldest loads of every
+  // wave.  (Without room for that copy, each wave loads the keys into its
+  // registers.)
   const uint8_t* const ksrc = reinterpret_cast<const uint8_t*>(a.k);
   KeyFrag<true, D> kf[NB];
   if constexpr (KLDS) {
@@ -141,18 +134,40 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
 #pragma unroll
   for (int k = 0; k < kRing - 1; ++k)
     if (k < my_tiles) issue(k);
-
-  // V and K rows in LDS (the first tiles may still be in flight), for every
-  // wave; then the W window keys as MFMA operands: block j holds key
-  // j*16 + col, dims 32 ks + 8 g4 .. +7
+  // the window's V rows into LDS (piece p of row r at r * PPR + p), after the
+  // first tiles, which the scoring needs first; used by the compaction only
+  uint8_t* const vbase = reinterpret_cast<uint8_t*>(a.v);
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int s0 = (wave * VI + i) * kWave, sp = s0 + lane;
+    tile_piece_to_lds(vbase + rows.at(t0 + sp / PPR) * 2 + (sp % PPR) * 16, vwin + s0 * 16);
+  }
+  // Loads retire in order: wait until only the n latest tiles (and, if v,
+  // the V rows issued after the first tiles) are in flight.
   static_assert(kRing == 4, "the waits count up to three tiles in flight");
-  if constexpr (KLDS) {
-    switch (min(my_tiles, kRing - 1)) {
-      case 3: wait_vm<3 * NI>(); break;
-      case 2: wait_vm<2 * NI>(); break;
-      case 1: wait_vm<NI>(); break;
-      default: wait_vm<0>(); break;
+  auto wait_tiles = [&](int n, bool v) {
+    if (v) {
+      switch (n) {
+        case 3: wait_vm<3 * NI + VI>(); break;
+        case 2: wait_vm<2 * NI + VI>(); break;
+        case 1: wait_vm<NI + VI>(); break;
+        default: wait_vm<VI>(); break;
+      }
+    } else {
+      switch (n) {
+        case 3: wait_vm<3 * NI>(); break;
+        case 2: wait_vm<2 * NI>(); break;
+        case 1: wait_vm<NI>(); break;
+        default: wait_vm<0>(); break;
+      }
     }
+  };
+
+  // K rows in LDS for every wave (the first tiles and the V rows may still
+  // be in flight); then the W window keys as MFMA operands: block j holds
+  // key j*16 + col, dims 32 ks + 8 g4 .. +7
+  if constexpr (KLDS) {
+    wait_tiles(min(my_tiles, kRing - 1), true);
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -170,14 +185,10 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
     for (int i = 0; i < 4; ++i) acc[j][i] = 0.f;
   for (int k = 0; k < my_tiles; ++k) {
     // tile k's loads are done once only the tiles issued after it are in
-    // flight (min(my_tiles - 1 - k, kRing - 1) of them)
+    // flight (min(my_tiles - 1 - k, kRing - 1) of them), and the V rows if
+    // they were issued after it (tiles 0 .. kRing - 2)
     if (k + kRing - 1 < my_tiles) issue(k + kRing - 1);
-    switch (min(my_tiles - 1 - k, kRing - 1)) {
-      case 3: wait_vm<3 * NI>(); break;
-      case 2: wait_vm<2 * NI>(); break;
-      case 1: wait_vm<NI>(); break;
-      default: wait_vm<0>(); break;
-    }
+    wait_tiles(min(my_tiles - 1 - k, kRing - 1), k < kRing - 1);
     const uint8_t* slot = ring[wave][k % kRing];
     bf16x8 qf[KS];
 #pragma unroll
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
     keep_s[slot] = t;
     krow[slot] = t0 + t;
   }
-  wait_vm<0>();      // this wave's V rows are in LDS (long done: they were its first loads)
+  wait_vm<0>();      // this wave's V rows are in LDS
   __syncthreads();   // slots, and every wave's V rows
 
   // compaction: row t0 + i <- row t0 + keep_s[i] for i < K, rows that move
