@@ -57,6 +57,29 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Four 16-byte LDS reads, waited for inside the block.  Written as one asm
+// block so that the compiler, which cannot tell these addresses apart from
+// the LDS that global_load_lds copies are still filling, does not make them
+// wait for every copy in flight; the caller orders them after the copies
+// they read (their own s_waitcnt vmcnt and a barrier).
+__device__ __forceinline__ void lds_read4(uint4 (&o)[4], uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <bool PAGED, int D, int NB>
 __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   constexpr int W = NB * kBlockKeys;
@@ -169,12 +192,22 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   if constexpr (KLDS) {
     wait_tiles(min(my_tiles, kRing - 1), true);
     lds_barrier();
+    // four 16-byte pieces per read block: one key block at head_dim 128,
+    // two at 64
+    static_assert((KS == 4 || KS == 2) && NB % 2 == 0, "whole read blocks");
+    constexpr int JB = 4 / KS;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int r = j * kBlockKeys + col;
+    for (int j0 = 0; j0 < NB; j0 += JB) {
+      uint32_t ad[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[j].w[ks] = *reinterpret_cast<const uint4*>(kwin + (r * PPR + ((4 * ks + g4) ^ (r % PPR))) * 16);
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + i / KS, ks = i % KS, r = j * kBlockKeys + col;
+        ad[i] = lds_addr(kwin + (r * PPR + ((4 * ks + g4) ^ (r % PPR))) * 16);
+      }
+      uint4 o[4];
+      lds_read4(o, ad[0], ad[1], ad[2], ad[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[j0 + i / KS].w[i % KS] = o[i];
     }
   }
 
