@@ -75,11 +75,6 @@ __device__ __forceinline__ void lds_read4(uint4 (&o)[4], uint32_t a0, uint32_t a
       : "memory");
 }
 
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 template <bool PAGED, int D, int NB>
 __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   constexpr int W = NB * kBlockKeys;
