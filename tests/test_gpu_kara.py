@@ -130,6 +130,14 @@ CONTIG = [
     (syn.config(1).with_(name="kara-d64", seed=72, num_seqs=3, num_layers=2, num_q_heads=16,
                          num_kv_heads=2, head_dim=64, lens=(300, 200, 250)),
      SimpleNamespace(window_len=64, keep=16, anchors=2, radius=1), (236, 100, 200)),
+    # head_dim 64 at the other two window lengths (2 and 8 key blocks; the
+    # window keys are read from LDS two blocks per read)
+    (syn.config(1).with_(name="kara-d64-w32", seed=78, num_seqs=3, num_layers=2, num_q_heads=8,
+                         num_kv_heads=2, head_dim=64, lens=(300, 200, 250)),
+     SimpleNamespace(window_len=32, keep=12, anchors=2, radius=2), (236, 100, 230)),
+    (syn.config(1).with_(name="kara-d64-w128", seed=79, num_seqs=3, num_layers=2, num_q_heads=16,
+                         num_kv_heads=2, head_dim=64, lens=(400, 300, 260)),
+     SimpleNamespace(window_len=128, keep=40, anchors=3, radius=2), (200, 172, 200)),
     (syn.config(1).with_(name="kara-w32-keep-all", seed=73, num_seqs=2, num_layers=2, num_q_heads=8,
                          num_kv_heads=8, lens=(96, 40)),
      SimpleNamespace(window_len=32, keep=32, anchors=0, radius=0), (64, 0)),
