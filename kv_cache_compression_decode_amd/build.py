@@ -34,9 +34,11 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-# per-source additions: the Gram kernel scales every matrix-core result on
-# the vector ALUs, so its MFMAs write ordinary VGPRs (no copy out of AGPRs)
-EXTRA_FLAGS = {"rkv_gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source additions: the Gram and KARA kernels use every matrix-core
+# result on the vector ALUs (column scaling; the window softmax), so their
+# MFMAs write ordinary VGPRs (no copy out of AGPRs)
+EXTRA_FLAGS = {"rkv_gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "rkv_kara.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd, verbose):
