@@ -57,22 +57,50 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Four 16-byte LDS reads, waited for inside the block.  Written as one asm
-// block so that the compiler, which cannot tell these addresses apart from
-// the LDS that global_load_lds copies are still filling, does not make them
-// wait for every copy in flight; the caller orders them after the copies
-// they read (their own s_waitcnt vmcnt and a barrier).
-__device__ __forceinline__ void lds_read4(uint4 (&o)[4], uint32_t a0, uint32_t a1, uint32_t a2,
-                                          uint32_t a3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
+// N 16-byte LDS reads at LDS byte addresses a, a + S, .., a + (N-1) S,
+// waited for inside the block.  Written as one asm block so that the
+// compiler, which cannot tell these addresses apart from the LDS that
+// global_load_lds copies are still filling, does not make them wait for
+// every copy in flight; the caller orders them after the copies they read
+// (their own s_waitcnt vmcnt and a barrier).
+template <int N, int S>
+__device__ __forceinline__ void lds_read_strided(uint4 (&o)[N], uint32_t a) {
+  static_assert(N == 2 || N == 4 || N == 8, "2, 4 or 8 reads");
+  static_assert(S % 16 == 0 && (N - 1) * S < 65536, "immediate offsets");
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:%3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1])
+        : "v"(a), "i"(S)
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:%5\n\t"
+        "ds_read_b128 %2, %4 offset:%6\n\t"
+        "ds_read_b128 %3, %4 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+        : "v"(a), "i"(S), "i"(2 * S), "i"(3 * S)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%9\n\t"
+        "ds_read_b128 %2, %8 offset:%10\n\t"
+        "ds_read_b128 %3, %8 offset:%11\n\t"
+        "ds_read_b128 %4, %8 offset:%12\n\t"
+        "ds_read_b128 %5, %8 offset:%13\n\t"
+        "ds_read_b128 %6, %8 offset:%14\n\t"
+        "ds_read_b128 %7, %8 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+          "=&v"(o[6]), "=&v"(o[7])
+        : "v"(a), "i"(S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S), "i"(7 * S)
+        : "memory");
+  }
 }
 
 template <bool PAGED, int D, int NB>
@@ -187,22 +215,16 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   if constexpr (KLDS) {
     wait_tiles(min(my_tiles, kRing - 1), true);
     lds_barrier();
-    // four 16-byte pieces per read block: one key block at head_dim 128,
-    // two at 64
-    static_assert((KS == 4 || KS == 2) && NB % 2 == 0, "whole read blocks");
-    constexpr int JB = 4 / KS;
+    // one read block per 32-dim slice: piece 4 ks + g4 of key j*16 + col sits
+    // at (j*16 + col) * PPR + ((4 ks + g4) ^ col) -- key block j a constant
+    // 16 rows further than block 0 (r % PPR = col for every block)
 #pragma unroll
-    for (int j0 = 0; j0 < NB; j0 += JB) {
-      uint32_t ad[4];
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 o[NB];
+      lds_read_strided<NB, kBlockKeys * PPR * 16>(
+          o, lds_addr(kwin + (col * PPR + ((4 * ks + g4) ^ (col % PPR))) * 16));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + i / KS, ks = i % KS, r = j * kBlockKeys + col;
-        ad[i] = lds_addr(kwin + (r * PPR + ((4 * ks + g4) ^ (r % PPR))) * 16);
-      }
-      uint4 o[4];
-      lds_read4(o, ad[0], ad[1], ad[2], ad[3]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kf[j0 + i / KS].w[i % KS] = o[i];
+      for (int j = 0; j < NB; ++j) kf[j].w[ks] = o[j];
     }
   }
 
