@@ -173,6 +173,10 @@ __device__ __forceinline__ void unit_score_span(const ScoreArgs& a, const Unit& 
   for (int rt = 0; rt < RT; ++rt) {
     if (rt >= rt1) continue;
     float mx = -INFINITY, zz = 0.f;
+    bf16x8 qf[KS];   // the tile's rows, read once for all key blocks
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
 #pragma unroll
     for (int j0 = 0; j0 < NBW; j0 += PH2) {
       if (j0 >= nbl) continue;
@@ -184,13 +188,11 @@ __device__ __forceinline__ void unit_score_span(const ScoreArgs& a, const Unit& 
       for (int j = 0; j < PH2; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {   // one 32-dim slice of the rows at a time
-        const bf16x8 qf =
-            *reinterpret_cast<const bf16x8*>(q_lds + (rt * 16 + col) * QP + 32 * ks + 8 * g4);
 #pragma unroll
         for (int j = 0; j < PH2; ++j)
           if (live[j])
             c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, kf[j0 + j].w[ks]), qf, c[j], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, kf[j0 + j].w[ks]), qf[ks], c[j], 0, 0, 0);
       }
       float cm = -INFINITY;   // max of the raw products (the scale a.c > 0 keeps the order)
 #pragma unroll
