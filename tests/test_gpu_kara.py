@@ -130,8 +130,8 @@ CONTIG = [
     (syn.config(1).with_(name="kara-d64", seed=72, num_seqs=3, num_layers=2, num_q_heads=16,
                          num_kv_heads=2, head_dim=64, lens=(300, 200, 250)),
      SimpleNamespace(window_len=64, keep=16, anchors=2, radius=1), (236, 100, 200)),
-    # head_dim 64 at the other two window lengths (2 and 8 key blocks; the
-    # window keys are read from LDS two blocks per read)
+    # head_dim 64 at the other two window lengths (2 and 8 key blocks in each
+    # strided LDS read of the window keys)
     (syn.config(1).with_(name="kara-d64-w32", seed=78, num_seqs=3, num_layers=2, num_q_heads=8,
                          num_kv_heads=2, head_dim=64, lens=(300, 200, 250)),
      SimpleNamespace(window_len=32, keep=12, anchors=2, radius=2), (236, 100, 230)),
