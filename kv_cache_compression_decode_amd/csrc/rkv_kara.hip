@@ -103,6 +103,28 @@ __device__ __forceinline__ void lds_read_strided(uint4 (&o)[N], uint32_t a) {
   }
 }
 
+// The value of lane l ^ j (j a power of two below 64; all lanes active) by
+// the cheapest exchange for the distance: DPP quad permutes for 1 and 2,
+// ds_swizzle's XOR mode (no LDS access) for 4 and 8, v_permlane16/32_swap
+// for 16 and 32 -- whose two outputs are a lane's own value and its
+// partner's, so their XOR with the own value is the partner's.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int j) {
+  switch (j) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);
+    case 8: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (8 << 10) | 0x1F);
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return p[0] ^ p[1] ^ v;
+    }
+    default: {   // 32
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return p[0] ^ p[1] ^ v;
+    }
+  }
+}
+
 template <bool PAGED, int D, int NB>
 __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   constexpr int W = NB * kBlockKeys;
@@ -301,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   // widened to +-radius; the other places go to the best outside the chunks.
   // A bitonic sort of the W composite keys (order key, then 255 - position:
   // unique, larger is better), one per thread of the first W, exchanges
-  // through lane shuffles (partner distance < 64) or LDS (64).  Sorted index
+  // across lanes (partner distance < 64, lane_xor) or through LDS (64).  Sorted index
   // = rank.  The fill takes the first K - |chunks| non-chunk tokens in that
   // order (a scan over the sorted positions).
   const int K = a.keep;
@@ -312,8 +334,8 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
       uint64_t other;
       if (j < kWave) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)ck, j);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(ck >> 32), j);
+        const uint32_t lo = lane_xor((uint32_t)ck, j);
+        const uint32_t hi = lane_xor((uint32_t)(ck >> 32), j);
         other = ((uint64_t)hi << 32) | lo;
       } else {
         __syncthreads();
