@@ -202,14 +202,19 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
 #pragma unroll
   for (int k = 0; k < kRing - 1; ++k)
     if (k < my_tiles) issue(k);
-  // the window's V rows into LDS (piece p of row r at r * PPR + p), after the
-  // first tiles, which the scoring needs first; used by the compaction only
+  // the window's V rows into LDS (piece p of row r at r * PPR + p); used by
+  // the compaction only, so issued after the first tile's products (before
+  // the loop in a wave without tiles), out of the start-up stream that the
+  // first products wait for
   uint8_t* const vbase = reinterpret_cast<uint8_t*>(a.v);
+  auto issue_v = [&] {
 #pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int s0 = (wave * VI + i) * kWave, sp = s0 + lane;
-    tile_piece_to_lds(vbase + rows.at(t0 + sp / PPR) * 2 + (sp % PPR) * 16, vwin + s0 * 16);
-  }
+    for (int i = 0; i < VI; ++i) {
+      const int s0 = (wave * VI + i) * kWave, sp = s0 + lane;
+      tile_piece_to_lds(vbase + rows.at(t0 + sp / PPR) * 2 + (sp % PPR) * 16, vwin + s0 * 16);
+    }
+  };
+  if (my_tiles == 0) issue_v();
   // Loads retire in order: wait until only the n latest tiles (and, if v,
   // the V rows issued after the first tiles) are in flight.
   static_assert(kRing == 4, "the waits count up to three tiles in flight");
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   // be in flight); then the W window keys as MFMA operands: block j holds
   // key j*16 + col, dims 32 ks + 8 g4 .. +7
   if constexpr (KLDS) {
-    wait_tiles(min(my_tiles, kRing - 1), true);
+    wait_tiles(min(my_tiles, kRing - 1), my_tiles == 0);
     lds_barrier();
     // one read block per 32-dim slice: piece 4 ks + g4 of key j*16 + col sits
     // at (j*16 + col) * PPR + ((4 ks + g4) ^ col) -- key block j a constant
@@ -258,9 +263,10 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
   for (int k = 0; k < my_tiles; ++k) {
     // tile k's loads are done once only the tiles issued after it are in
     // flight (min(my_tiles - 1 - k, kRing - 1) of them), and the V rows if
-    // they were issued after it (tiles 0 .. kRing - 2)
+    // they were issued after it (at the end of iteration 0, after tiles
+    // 0 .. min(kRing, my_tiles) - 1)
     if (k + kRing - 1 < my_tiles) issue(k + kRing - 1);
-    wait_tiles(min(my_tiles - 1 - k, kRing - 1), k < kRing - 1);
+    wait_tiles(min(my_tiles - 1 - k, kRing - 1), k >= 1 && k < min(kRing, my_tiles));
     const uint8_t* slot = ring[wave][k % kRing];
     bf16x8 qf[KS];
 #pragma unroll
@@ -299,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void kara_step_kernel(KaraArgs a) {
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(e[j][i], inv, acc[j][i]);
+    if (k == 0) issue_v();
   }
   // per key: the sum over this wave's rows (the 16 lanes of a DPP row hold
   // the 16 rows of each tile), then over the waves

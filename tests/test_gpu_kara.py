@@ -138,6 +138,11 @@ CONTIG = [
     (syn.config(1).with_(name="kara-d64-w128", seed=79, num_seqs=3, num_layers=2, num_q_heads=16,
                          num_kv_heads=2, head_dim=64, lens=(400, 300, 260)),
      SimpleNamespace(window_len=128, keep=40, anchors=3, radius=2), (200, 172, 200)),
+    # G 1 at head_dim 64: two query tiles, so two waves score none (their V
+    # rows are copied before the tile loop) while the keys go through LDS
+    (syn.config(1).with_(name="kara-d64-w32-g1", seed=80, num_seqs=2, num_layers=2, num_q_heads=4,
+                         num_kv_heads=4, head_dim=64, lens=(160, 90)),
+     SimpleNamespace(window_len=32, keep=10, anchors=1, radius=3), (100, 40)),
     (syn.config(1).with_(name="kara-w32-keep-all", seed=73, num_seqs=2, num_layers=2, num_q_heads=8,
                          num_kv_heads=8, lens=(96, 40)),
      SimpleNamespace(window_len=32, keep=32, anchors=0, radius=0), (64, 0)),
